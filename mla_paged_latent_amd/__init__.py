@@ -1,0 +1,185 @@
+"""MLA decode over a paged latent KV cache on MI355X (gfx950).
+
+Thin ctypes binding of the C ABI in include/mla_paged_latent.h. Each Python
+function has the name of the C entry point it calls and only marshals
+arguments: every step of the computation runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream. The library must be
+built first (python -m mla_paged_latent_amd.build); nothing here falls back to
+another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import numpy as np
+
+LIB_PATH = Path(__file__).resolve().parent / "libmla_paged_latent.so"
+
+D_QK = 576
+D_V = 512
+PAGE_SIZE = 64
+META_INTS = 8
+
+MLA_OK = 0
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (func, status_string(status), status))
+
+
+def load_library(path: Path | str | None = None):
+    """Load the built HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise RuntimeError("HIP library %s is not built; run `python -m mla_paged_latent_amd.build`" % p)
+    lib = ctypes.CDLL(str(p))
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_plan_sizes.restype = i32
+    lib.mla_plan_sizes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(sz),
+                                   ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.mla_workspace_bytes.restype = i32
+    lib.mla_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.mla_get_metadata.restype = i32
+    lib.mla_get_metadata.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_get_metadata_host.restype = i32
+    lib.mla_get_metadata_host.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    lib.mla_decode_fwd.restype = i32
+    lib.mla_decode_fwd.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, ctypes.c_float, i32,
+                                   vp, vp, i32, vp, vp, vp, sz, vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mla_status_string(int(status)).decode()
+
+
+def _check(func: str, rc: int):
+    if rc != MLA_OK:
+        raise MLAError(func, rc)
+
+
+def mla_plan_sizes(batch: int, s_q: int, h_q: int, num_cus: int = 0) -> dict:
+    """Plan geometry and buffer sizes (host only). num_cus <= 0 asks the current device."""
+    lib = load_library()
+    units = ctypes.c_int(0)
+    meta, splits, ws = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mla_plan_sizes", lib.mla_plan_sizes(batch, s_q, h_q, num_cus, ctypes.byref(units),
+                                                ctypes.byref(meta), ctypes.byref(splits), ctypes.byref(ws)))
+    return {"num_units": units.value, "meta_bytes": meta.value, "splits_bytes": splits.value,
+            "workspace_bytes": ws.value}
+
+
+def _stream(torch):
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def mla_workspace_bytes(batch: int, s_q: int, h_q: int, num_units: int) -> int:
+    return workspace_bytes(batch, s_q, h_q, num_units)
+
+
+def mla_get_metadata(cache_seqlens, h_q: int, s_q: int = 1, num_units: int | None = None):
+    """Split-KV tile plan on the device. Returns (tile_meta int32 [G, 8], num_splits int32 [B+1])."""
+    import torch
+    _need(cache_seqlens, torch.int32, "cache_seqlens")
+    B = int(cache_seqlens.shape[0])
+    with torch.cuda.device(cache_seqlens.device):
+        if num_units is None:
+            num_units = mla_plan_sizes(B, s_q, h_q)["num_units"]
+        meta = torch.empty((num_units, META_INTS), dtype=torch.int32, device=cache_seqlens.device)
+        splits = torch.empty((B + 1,), dtype=torch.int32, device=cache_seqlens.device)
+        _check("mla_get_metadata", load_library().mla_get_metadata(
+            cache_seqlens.data_ptr(), B, s_q, h_q, num_units, meta.data_ptr(), splits.data_ptr(), _stream(torch)))
+    return meta, splits
+
+
+def mla_get_metadata_host(cache_seqlens, h_q: int, s_q: int, num_units: int):
+    """The same plan computed by the library on the host (numpy in, numpy out)."""
+    lens = np.ascontiguousarray(np.asarray(cache_seqlens), dtype=np.int32)
+    B = int(lens.shape[0])
+    meta = np.zeros((num_units, META_INTS), dtype=np.int32)
+    splits = np.zeros((B + 1,), dtype=np.int32)
+    _check("mla_get_metadata_host", load_library().mla_get_metadata_host(
+        lens.ctypes.data, B, s_q, h_q, num_units, meta.ctypes.data, splits.ctypes.data))
+    return meta, splits
+
+
+def mla_decode_fwd(q, kcache, block_table, cache_seqlens, softmax_scale: float, tile_meta, num_splits,
+                   causal: bool = True, out=None, lse=None, workspace=None):
+    """Decode attention. q bf16 [B, s_q, h_q, 576], kcache bf16 [nblocks, 64, 576],
+    block_table int32 [B, max_blocks], cache_seqlens int32 [B].
+    Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, s_q, h_q])."""
+    import torch
+    _need(q, torch.bfloat16, "q")
+    dev = q.device
+    _need(kcache, torch.bfloat16, "kcache", dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    _need(cache_seqlens, torch.int32, "cache_seqlens", dev)
+    _need(tile_meta, torch.int32, "tile_meta", dev)
+    _need(num_splits, torch.int32, "num_splits", dev)
+    if q.dim() != 4 or q.shape[3] != D_QK:
+        raise ValueError("q must be [B, s_q, h_q, 576]")
+    if kcache.dim() != 3 or kcache.shape[1] != PAGE_SIZE or kcache.shape[2] != D_QK:
+        raise ValueError("kcache must be [nblocks, 64, 576]")
+    B, s_q, h_q, _ = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and cache_seqlens [B]")
+    if tile_meta.dim() != 2 or tile_meta.shape[1] != META_INTS or tuple(num_splits.shape) != (B + 1,):
+        raise ValueError("tile_meta / num_splits do not look like a plan for this batch")
+    num_units = int(tile_meta.shape[0])
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((B, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+        _need(out, torch.bfloat16, "out", dev)
+        _need(lse, torch.float32, "lse", dev)
+        if tuple(out.shape) != (B, s_q, h_q, D_V) or tuple(lse.shape) != (B, s_q, h_q):
+            raise ValueError("out / lse have the wrong shape")
+        if workspace is None:
+            ws_bytes = workspace_bytes(B, s_q, h_q, num_units)
+            workspace = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        _need(workspace, torch.uint8, "workspace", dev)
+        _check("mla_decode_fwd", load_library().mla_decode_fwd(
+            q.data_ptr(), kcache.data_ptr(), int(kcache.shape[0]), block_table.data_ptr(),
+            int(block_table.shape[1]), cache_seqlens.data_ptr(), B, s_q, h_q, float(softmax_scale),
+            1 if causal else 0, tile_meta.data_ptr(), num_splits.data_ptr(), num_units,
+            out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), int(workspace.numel()), _stream(torch)))
+    return out, lse
+
+
+def workspace_bytes(batch: int, s_q: int, h_q: int, num_units: int) -> int:
+    """Workspace mla_decode_fwd needs for a plan of num_units units (asks the library)."""
+    n = ctypes.c_size_t(0)
+    _check("mla_workspace_bytes", load_library().mla_workspace_bytes(batch, s_q, h_q, num_units, ctypes.byref(n)))
+    return n.value
+
+
+__all__ = ["mla_plan_sizes", "mla_workspace_bytes", "mla_get_metadata", "mla_get_metadata_host", "mla_decode_fwd",
+           "workspace_bytes", "load_library", "status_string", "MLAError", "LIB_PATH",
+           "D_QK", "D_V", "PAGE_SIZE", "META_INTS"]

@@ -1,0 +1,186 @@
+// C ABI of the library: host-side argument checks, buffer sizing and kernel
+// launches. Every check runs before anything is enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mla_paged_latent.h"
+#include "mla_common.h"
+
+namespace mla {
+void plan_host(const int32_t* seqlens, int batch, int kappa, int num_units, int32_t* meta, int32_t* splits);
+hipError_t launch_plan(const int32_t* seqlens, int batch, int kappa, int num_units, int32_t* meta,
+                       int32_t* splits, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+}  // namespace mla
+
+namespace {
+
+constexpr int kMaxBatch = 16384;     // the device planner keeps two int arrays of batch+1 in LDS
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int check_shape(int batch, int s_q, int h_q)
+{
+    if (batch < 1 || s_q < 1 || h_q < 1) return MLA_ERR_INVALID_ARG;
+    if (batch > kMaxBatch) return MLA_ERR_UNSUPPORTED;
+    const long rows = (long)s_q * h_q;
+    if (rows % 16 != 0 || rows > mla::kMaxRows) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
+struct Geometry {
+    int rows_total, rows_wg, head_groups, kappa;
+};
+
+Geometry geometry(int s_q, int h_q)
+{
+    Geometry g;
+    g.rows_total = s_q * h_q;
+    g.rows_wg = mla::rows_per_wg(g.rows_total);
+    g.head_groups = g.rows_total / g.rows_wg;
+    g.kappa = mla::segment_cost(g.rows_wg);
+    return g;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace: partial outputs for at most num_units + batch (unit, sequence)
+// segments -- each unit boundary adds at most one segment to a sequence.
+void workspace_layout(int batch, int rows_total, int num_units, size_t* part_o_bytes, size_t* total)
+{
+    const size_t slots = (size_t)num_units + (size_t)batch;
+    *part_o_bytes = round_up(slots * rows_total * mla::kDv * sizeof(float), 256);
+    *total = *part_o_bytes + round_up(slots * rows_total * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status)
+{
+    switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, or non-positive size)";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape (s_q*h_q must be a multiple of 16 in [16, 1024], batch <= 16384)";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mla_plan_sizes reports";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int mla_plan_sizes(int batch, int s_q, int h_q, int num_cus, int* num_units, size_t* meta_bytes,
+                   size_t* splits_bytes, size_t* workspace_bytes)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (num_cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+        if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return MLA_ERR_HIP;
+        if (num_cus <= 0) return MLA_ERR_HIP;
+    }
+    const Geometry geo = geometry(s_q, h_q);
+    // one workgroup per CU (the block buffers fill most of the LDS)
+    int units = num_cus / geo.head_groups;
+    if (units < 1) units = 1;
+    size_t part_o = 0, total = 0;
+    workspace_layout(batch, geo.rows_total, units, &part_o, &total);
+    if (num_units) *num_units = units;
+    if (meta_bytes) *meta_bytes = (size_t)units * MLA_META_INTS * sizeof(int32_t);
+    if (splits_bytes) *splits_bytes = (size_t)(batch + 1) * sizeof(int32_t);
+    if (workspace_bytes) *workspace_bytes = total;
+    return MLA_OK;
+}
+
+int mla_workspace_bytes(int batch, int s_q, int h_q, int num_units, size_t* workspace_bytes)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (num_units < 1 || !workspace_bytes) return MLA_ERR_INVALID_ARG;
+    size_t part_o = 0;
+    workspace_layout(batch, s_q * h_q, num_units, &part_o, workspace_bytes);
+    return MLA_OK;
+}
+
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_units,
+                     int32_t* tile_meta, int32_t* num_splits, void* stream)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (!cache_seqlens || !tile_meta || !num_splits || num_units < 1) return MLA_ERR_INVALID_ARG;
+    const Geometry geo = geometry(s_q, h_q);
+    if (mla::launch_plan(cache_seqlens, batch, geo.kappa, num_units, tile_meta, num_splits,
+                         (hipStream_t)stream) != hipSuccess)
+        return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_get_metadata_host(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_units,
+                          int32_t* tile_meta, int32_t* num_splits)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (!cache_seqlens || !tile_meta || !num_splits || num_units < 1) return MLA_ERR_INVALID_ARG;
+    const Geometry geo = geometry(s_q, h_q);
+    mla::plan_host(cache_seqlens, batch, geo.kappa, num_units, tile_meta, num_splits);
+    return MLA_OK;
+}
+
+int mla_decode_fwd(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table,
+                   int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                   float softmax_scale, int causal, const int32_t* tile_meta, const int32_t* num_splits,
+                   int num_units, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (!q || !kcache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse ||
+        !workspace)
+        return MLA_ERR_INVALID_ARG;
+    if (nblocks < 1 || max_blocks < 1 || num_units < 1 || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(out) || !aligned16(workspace) || ((uintptr_t)lse & 3u))
+        return MLA_ERR_INVALID_ARG;
+    const Geometry geo = geometry(s_q, h_q);
+    size_t part_o = 0, total = 0;
+    workspace_layout(batch, geo.rows_total, num_units, &part_o, &total);
+    if (workspace_bytes < total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    mla::DecodeParams p;
+    p.q = (const uint16_t*)q;
+    p.kcache = (const uint16_t*)kcache;
+    p.block_table = block_table;
+    p.seqlens = cache_seqlens;
+    p.meta = tile_meta;
+    p.splits = num_splits;
+    p.out = (uint16_t*)out;
+    p.lse = lse;
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)((char*)workspace + part_o);
+    p.nblocks = nblocks;
+    p.max_blocks = max_blocks;
+    p.batch = batch;
+    p.s_q = s_q;
+    p.h_q = h_q;
+    p.rows_total = geo.rows_total;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+
+    hipStream_t st = (hipStream_t)stream;
+    if (mla::launch_decode(p, num_units, geo.head_groups, geo.rows_wg, st) != hipSuccess) return MLA_ERR_HIP;
+
+    mla::CombineParams c;
+    c.splits = num_splits;
+    c.part_o = p.part_o;
+    c.part_lse = p.part_lse;
+    c.out = p.out;
+    c.lse = lse;
+    c.batch = batch;
+    c.rows_total = geo.rows_total;
+    if (mla::launch_combine(c, st) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+}  // extern "C"

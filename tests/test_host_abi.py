@@ -1,0 +1,185 @@
+"""Host-side tests of the C ABI (no GPU): symbols, argument checks, the host planner.
+
+The library is loaded but no device work is requested: every call here either
+fails its host-side checks before any HIP call or runs purely on the host.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import mla_paged_latent_amd as mla
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "mla_paged_latent.h"
+
+MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL = -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not mla.LIB_PATH.exists():
+        from mla_paged_latent_amd import build
+        build.build()
+    return mla.load_library()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_two_calls():
+    fns = declared_functions()
+    assert "mla_get_metadata" in fns and "mla_decode_fwd" in fns, fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_no_torch_types_in_the_abi():
+    text = HEADER.read_text()
+    assert "torch" not in re.sub(r"/\*.*?\*/", "", text, flags=re.S).lower()
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 99):
+        assert lib.mla_status_string(code)
+
+
+def _decode_args(**over):
+    fake = ctypes.c_void_p(0x10000)      # never dereferenced: the checks fail first
+    a = dict(q=fake, kcache=fake, nblocks=8, block_table=fake, max_blocks=4, cache_seqlens=fake, batch=2,
+             s_q=1, h_q=16, scale=0.07, causal=1, meta=fake, splits=fake, units=8, out=fake, lse=fake,
+             ws=fake, ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    return [a[k] for k in ("q", "kcache", "nblocks", "block_table", "max_blocks", "cache_seqlens", "batch",
+                           "s_q", "h_q", "scale", "causal", "meta", "splits", "units", "out", "lse", "ws",
+                           "ws_bytes", "stream")]
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), MLA_ERR_INVALID_ARG),
+    (dict(kcache=None), MLA_ERR_INVALID_ARG),
+    (dict(out=None), MLA_ERR_INVALID_ARG),
+    (dict(ws=None), MLA_ERR_INVALID_ARG),
+    (dict(batch=0), MLA_ERR_INVALID_ARG),
+    (dict(nblocks=0), MLA_ERR_INVALID_ARG),
+    (dict(max_blocks=0), MLA_ERR_INVALID_ARG),
+    (dict(units=0), MLA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), MLA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), MLA_ERR_INVALID_ARG),
+    (dict(q=ctypes.c_void_p(0x10008)), MLA_ERR_INVALID_ARG),      # misaligned
+    (dict(h_q=15), MLA_ERR_UNSUPPORTED),
+    (dict(s_q=3, h_q=8), MLA_ERR_UNSUPPORTED),                    # 24 rows
+    (dict(s_q=16, h_q=128), MLA_ERR_UNSUPPORTED),                 # 2048 rows
+    (dict(batch=16385), MLA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=1024), MLA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_rejects_bad_arguments_before_any_launch(lib, over, code):
+    assert lib.mla_decode_fwd(*_decode_args(**over)) == code
+
+
+def test_get_metadata_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.mla_get_metadata(None, 2, 1, 16, 8, fake, fake, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_get_metadata(fake, 2, 1, 16, 0, fake, fake, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_get_metadata(fake, 2, 1, 17, 8, fake, fake, None) == MLA_ERR_UNSUPPORTED
+
+
+def test_plan_sizes(lib):
+    s = mla.mla_plan_sizes(16, 1, 16, num_cus=256)
+    assert s["num_units"] == 256
+    assert s["meta_bytes"] == 256 * 8 * 4 and s["splits_bytes"] == 17 * 4
+    assert s["workspace_bytes"] == mla.mla_workspace_bytes(16, 1, 16, 256)
+    # h_q=128, s_q=2: 256 rows = two head groups of 128, so half the units
+    assert mla.mla_plan_sizes(128, 2, 128, num_cus=256)["num_units"] == 128
+    with pytest.raises(mla.MLAError):
+        mla.mla_plan_sizes(4, 1, 10, num_cus=256)
+
+
+# ------------------------------------------------------------- planner properties
+
+def blocks(L):
+    return (np.asarray(L, dtype=np.int64) + 63) // 64
+
+
+def check_plan(lens, s_q, h_q, units, meta, splits):
+    """Every block owned by exactly one unit, units contiguous, split counts consistent, balance bound."""
+    lens = np.asarray(lens)
+    B = len(lens)
+    nb = blocks(lens)
+    owner = {}
+    touched = [set() for _ in range(B)]
+    rows = s_q * h_q
+    rows_wg = 128 if rows % 128 == 0 else 64 if rows % 64 == 0 else 32 if rows % 32 == 0 else 16
+    kappa = 1 + rows_wg // 32
+    total = int(nb.sum()) + kappa * int((nb > 0).sum())
+    W = max(1, -(-total // units))
+    for u in range(units):
+        b0, j0, b1, j1, split = (int(x) for x in meta[u, :5])
+        assert (b0, j0) <= (b1, j1)
+        cost = 0
+        first = True
+        b, j = b0, j0
+        while (b, j) < (b1, j1) and b < B:
+            if j >= nb[b]:
+                b, j = b + 1, 0
+                continue
+            assert (b, j) not in owner
+            owner[(b, j)] = u
+            if u not in touched[b]:
+                touched[b].add(u)
+                cost += kappa
+                if first:
+                    # the split index of the first segment counts earlier units on b
+                    assert split == len([x for x in touched[b] if x < u])
+                first = False
+            cost += 1
+            j += 1
+        assert cost <= W + kappa, (u, cost, W)
+    for b in range(B):
+        for j in range(int(nb[b])):
+            assert (b, j) in owner, (b, j)
+        # a sequence's blocks go to non-decreasing units
+        us = [owner[(b, j)] for j in range(int(nb[b]))]
+        assert us == sorted(us)
+    ns = np.array([len(t) for t in touched])
+    assert splits[0] == 0 and np.array_equal(np.diff(splits), ns)
+    assert splits[-1] <= units + B
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_host_plan_properties(lib, seed):
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 300))
+    lens = rng.integers(0, 5000, B)
+    lens[rng.random(B) < 0.1] = 0
+    s_q, h_q = [(1, 16), (2, 16), (1, 128), (2, 128), (3, 16), (1, 32), (2, 32)][seed % 7]
+    units = int(rng.choice([1, 3, 64, 128, 256, 1000]))
+    meta, splits = mla.mla_get_metadata_host(lens, h_q, s_q, units)
+    check_plan(lens, s_q, h_q, units, meta, splits)
+
+
+def test_host_plan_workloads(lib):
+    import workloads as wl
+    for name in wl.WORKLOADS:
+        rng = np.random.default_rng(wl.WORKLOADS[name])
+        lens = wl._seqlens(name, rng)
+        s_q, h_q, _ = wl._shape(name)
+        units = mla.mla_plan_sizes(len(lens), s_q, h_q, num_cus=256)["num_units"]
+        meta, splits = mla.mla_get_metadata_host(lens, h_q, s_q, units)
+        check_plan(lens, s_q, h_q, units, meta, splits)
+
+
+def test_host_plan_all_empty(lib):
+    meta, splits = mla.mla_get_metadata_host([0, 0, 0], 16, 1, 8)
+    assert np.array_equal(splits, [0, 0, 0, 0])
+    assert (meta[:, 0] == 3).all()          # every unit starts past the batch
