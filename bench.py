@@ -1,0 +1,226 @@
+"""Benchmark: MLA decode over a paged bf16 latent cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload memory_bound]
+
+One step is one pass of the whole decode path over one synthetic batch:
+mla_get_metadata (split-KV plan) + mla_decode_fwd (decode, split merge).
+W untimed steps, then K timed steps between device synchronisations. Each
+step reads a different replica of (kcache, block_table, q), and the replicas
+together exceed twice the 256 MB Infinity Cache, so the cache is read from
+HBM. Prints one JSON line.
+
+value = algorithmic bytes per step / step time (GB/s); algorithmic bytes
+count each cached row once plus q, out, lse, the used block-table entries and
+cache_seqlens. tflops = (QK^T + PV MAC flops) / step time. The roofline entry
+is for the decode kernel alone, timed with events on its stream around every
+mla_decode_fwd call in the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
+MALL_BYTES = 256 * 2 ** 20
+DECODE_SRC = os.path.join(ROOT, "mla_paged_latent_amd", "csrc", "mla_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
+    were taken on the current decode kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = doc.get(workload)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, nbytes_total, min_seconds=10.0, max_reps=50):
+    """The oracle, as it is, on the host cores: whole batches until min_seconds have passed."""
+    import oracle
+    threads = oracle.default_threads()
+    oracle.load()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode_inputs(inp, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    per = el / reps
+    return {"value": round(nbytes_total / per / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "tflops": round(inp_flops(inp) / per / 1e12, 6),
+            "sample": "%d full passes over the %s batch (B=%d), %.1f s wall, float64 oracle"
+                      % (reps, inp.name, inp.batch, el)}
+
+
+def inp_flops(inp):
+    return wl.algorithmic_counts(inp.cache_seqlens, inp.s_q, inp.h_q, inp.causal)[1]
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="memory_bound", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 2x the 256 MB cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for counter calibration) and exit")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import mla_paged_latent_amd as mla
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return 0
+
+    mla.load_library()
+    inp = wl.make_workload(args.workload, poison=False)
+    B, s_q, h_q = inp.batch, inp.s_q, inp.h_q
+    nbytes, flops = wl.algorithmic_counts(inp.cache_seqlens, s_q, h_q, inp.causal)
+    replica_bytes = inp.kcache.nbytes + inp.q.nbytes + inp.block_table.nbytes
+    R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / replica_bytes))
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base_k, base_q = bf16(inp.kcache), bf16(inp.q)
+    base_t = torch.from_numpy(inp.block_table).to(dev)
+    lens = torch.from_numpy(inp.cache_seqlens).to(dev)
+    reps = [(base_k.clone(), base_q.clone(), base_t.clone(), lens.clone()) for _ in range(R)]
+    del base_k, base_q, base_t
+
+    sizes = mla.mla_plan_sizes(B, s_q, h_q)
+    units = sizes["num_units"]
+    out = torch.empty((B, s_q, h_q, mla.D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+    ws = torch.empty((sizes["workspace_bytes"],), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        kc, q, tab, ln = reps[k % R]
+        meta, splits = mla.mla_get_metadata(ln, h_q, s_q, num_units=units)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_decode_fwd(q, kc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal,
+                           out=out, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(k, evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    dec_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    k_gbs = nbytes / (dec_avg * 1e-3) / 1e9
+    k_tf = flops / (dec_avg * 1e-3) / 1e12
+    traffic = measured_traffic(args.workload)
+
+    result = {
+        "metric": "MLA decode TFLOPS + HBM GB/s (fraction of MI355X peak), paged bf16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %s, d_qk=576, d_v=512, block 64, shuffled block_table, bf16 N(0,1), "
+                               "scale 1/sqrt(192)" % (args.workload, wl.DESCRIPTIONS[args.workload]),
+                   "batch": B, "s_q": s_q, "h_q": h_q, "tokens": int(inp.cache_seqlens.sum()),
+                   "replicas": R, "num_units": units},
+        "tflops": round(tflops, 3),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+        "alg_bytes_per_step": nbytes,
+        "alg_flops_per_step": flops,
+        "roofline": {
+            "bound": "hbm" if flops / nbytes < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma",
+            "kernel": "mla_decode_fwd (decode kernel)",
+            "achieved": round(k_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_ms_avg": round(dec_avg, 6),
+            "kernel_ms_median": round(dec_ms[len(dec_ms) // 2], 6),
+            "kernel_tflops": round(k_tf, 3),
+            "kernel_mfma_frac": round(k_tf / BF16_PEAK_TFLOPS, 5),
+        },
+    }
+    if result["roofline"]["bound"] == "mfma":
+        r = result["roofline"]
+        r.update({"achieved": round(k_tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(k_tf / BF16_PEAK_TFLOPS, 5), "kernel_gbs": round(k_gbs, 2)})
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, nbytes, min_seconds=args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

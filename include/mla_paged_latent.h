@@ -94,9 +94,13 @@ int mla_workspace_bytes(int batch, int s_q, int h_q, int num_units, size_t* work
 /*
  * Split-KV tile plan for a variable-length batch (the pages only say the
  * kernel is tuned for variable-length serving: GeekNews release note).
- * The batch's cache blocks, taken in (sequence, block) order with a fixed
- * extra cost per sequence, are cut into num_units contiguous runs of near
- * equal cost; each run is one workgroup's work.
+ * Each unit is one workgroup's run of cache blocks, contiguous in (sequence,
+ * block) order; every block belongs to exactly one unit. When s_q*h_q is a
+ * multiple of 128 the blocks, with a fixed extra cost per sequence, are cut
+ * into num_units runs of near-equal cost (a run may span sequences);
+ * otherwise each sequence is cut into near-equal runs of at most
+ * ceil(total_blocks / (num_units - batch)) blocks, and num_units must be at
+ * least batch + 1.
  *   cache_seqlens: device int32 [batch].
  *   tile_meta: device int32 [num_units, MLA_META_INTS], written. Row u is
  *     {b_begin, blk_begin, b_end, blk_end, split_index, 0, 0, 0}: unit u
@@ -137,7 +141,8 @@ int mla_get_metadata_host(const int32_t* cache_seqlens, int batch, int s_q, int 
  * Enqueues the decode kernel and the split combine kernel on `stream`.
  * Calls that share a workspace must not overlap in time.
  * Errors: MLA_ERR_INVALID_ARG (null or misaligned pointer, batch < 1,
- *   nblocks < 1, max_blocks < 1, num_units < 1, non-finite scale),
+ *   nblocks < 1, max_blocks < 1, num_units too small for the plan shape,
+ *   non-finite scale),
  *   MLA_ERR_UNSUPPORTED (s_q*h_q), MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP.
  */
 int mla_decode_fwd(const void* q, const void* kcache, int64_t nblocks,
@@ -147,6 +152,27 @@ int mla_decode_fwd(const void* q, const void* kcache, int64_t nblocks,
                    const int32_t* tile_meta, const int32_t* num_splits, int num_units,
                    void* out, float* lse, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * The two stages of mla_decode_fwd as separate calls (same arguments and
+ * checks), for callers that time or schedule the two kernels apart:
+ * mla_decode_fwd is exactly mla_decode_fwd_splits followed by
+ * mla_combine_splits on the same stream with the same workspace.
+ * mla_decode_fwd_splits writes out/lse of sequences the plan did not split
+ * and leaves fp32 partial results of split ones in the workspace;
+ * mla_combine_splits merges those partials by their log-sum-exp (and writes
+ * out = 0, lse = -inf for sequences with no cached token).
+ */
+int mla_decode_fwd_splits(const void* q, const void* kcache, int64_t nblocks,
+                          const int32_t* block_table, int max_blocks,
+                          const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                          float softmax_scale, int causal,
+                          const int32_t* tile_meta, const int32_t* num_splits, int num_units,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, int num_units,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -53,9 +53,12 @@ def load_library(path: Path | str | None = None):
     lib.mla_get_metadata.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_get_metadata_host.restype = i32
     lib.mla_get_metadata_host.argtypes = [vp, i32, i32, i32, i32, vp, vp]
-    lib.mla_decode_fwd.restype = i32
-    lib.mla_decode_fwd.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, ctypes.c_float, i32,
-                                   vp, vp, i32, vp, vp, vp, sz, vp]
+    dec = [vp, vp, i64, vp, i32, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, i32, vp, vp, vp, sz, vp]
+    for name in ("mla_decode_fwd", "mla_decode_fwd_splits"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = dec
+    lib.mla_combine_splits.restype = i32
+    lib.mla_combine_splits.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     if path is None:
         _lib = lib
     return lib
@@ -129,11 +132,8 @@ def mla_get_metadata_host(cache_seqlens, h_q: int, s_q: int, num_units: int):
     return meta, splits
 
 
-def mla_decode_fwd(q, kcache, block_table, cache_seqlens, softmax_scale: float, tile_meta, num_splits,
-                   causal: bool = True, out=None, lse=None, workspace=None):
-    """Decode attention. q bf16 [B, s_q, h_q, 576], kcache bf16 [nblocks, 64, 576],
-    block_table int32 [B, max_blocks], cache_seqlens int32 [B].
-    Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, s_q, h_q])."""
+def _decode_args(q, kcache, block_table, cache_seqlens, softmax_scale, tile_meta, num_splits, causal, out, lse,
+                 workspace):
     import torch
     _need(q, torch.bfloat16, "q")
     dev = q.device
@@ -152,24 +152,59 @@ def mla_decode_fwd(q, kcache, block_table, cache_seqlens, softmax_scale: float, 
     if tile_meta.dim() != 2 or tile_meta.shape[1] != META_INTS or tuple(num_splits.shape) != (B + 1,):
         raise ValueError("tile_meta / num_splits do not look like a plan for this batch")
     num_units = int(tile_meta.shape[0])
-    with torch.cuda.device(dev):
-        if out is None:
-            out = torch.empty((B, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
-        if lse is None:
-            lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
-        _need(out, torch.bfloat16, "out", dev)
-        _need(lse, torch.float32, "lse", dev)
-        if tuple(out.shape) != (B, s_q, h_q, D_V) or tuple(lse.shape) != (B, s_q, h_q):
-            raise ValueError("out / lse have the wrong shape")
-        if workspace is None:
-            ws_bytes = workspace_bytes(B, s_q, h_q, num_units)
-            workspace = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
-        _need(workspace, torch.uint8, "workspace", dev)
-        _check("mla_decode_fwd", load_library().mla_decode_fwd(
-            q.data_ptr(), kcache.data_ptr(), int(kcache.shape[0]), block_table.data_ptr(),
-            int(block_table.shape[1]), cache_seqlens.data_ptr(), B, s_q, h_q, float(softmax_scale),
-            1 if causal else 0, tile_meta.data_ptr(), num_splits.data_ptr(), num_units,
-            out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), int(workspace.numel()), _stream(torch)))
+    if out is None:
+        out = torch.empty((B, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+    _need(out, torch.bfloat16, "out", dev)
+    _need(lse, torch.float32, "lse", dev)
+    if tuple(out.shape) != (B, s_q, h_q, D_V) or tuple(lse.shape) != (B, s_q, h_q):
+        raise ValueError("out / lse have the wrong shape")
+    if workspace is None:
+        ws_bytes = workspace_bytes(B, s_q, h_q, num_units)
+        workspace = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, "workspace", dev)
+    args = (q.data_ptr(), kcache.data_ptr(), int(kcache.shape[0]), block_table.data_ptr(), int(block_table.shape[1]),
+            cache_seqlens.data_ptr(), B, s_q, h_q, float(softmax_scale), 1 if causal else 0, tile_meta.data_ptr(),
+            num_splits.data_ptr(), num_units, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+            int(workspace.numel()), _stream(torch))
+    return args, out, lse, workspace
+
+
+def mla_decode_fwd(q, kcache, block_table, cache_seqlens, softmax_scale: float, tile_meta, num_splits,
+                   causal: bool = True, out=None, lse=None, workspace=None):
+    """Decode attention. q bf16 [B, s_q, h_q, 576], kcache bf16 [nblocks, 64, 576],
+    block_table int32 [B, max_blocks], cache_seqlens int32 [B].
+    Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, s_q, h_q])."""
+    import torch
+    with torch.cuda.device(q.device):
+        args, out, lse, _ = _decode_args(q, kcache, block_table, cache_seqlens, softmax_scale, tile_meta,
+                                         num_splits, causal, out, lse, workspace)
+        _check("mla_decode_fwd", load_library().mla_decode_fwd(*args))
+    return out, lse
+
+
+def mla_decode_fwd_splits(q, kcache, block_table, cache_seqlens, softmax_scale: float, tile_meta, num_splits,
+                          causal: bool = True, out=None, lse=None, workspace=None):
+    """First stage of mla_decode_fwd only (the decode kernel): unsplit sequences get
+    out/lse, split ones leave partials in workspace. Returns (out, lse, workspace)."""
+    import torch
+    with torch.cuda.device(q.device):
+        args, out, lse, workspace = _decode_args(q, kcache, block_table, cache_seqlens, softmax_scale, tile_meta,
+                                                 num_splits, causal, out, lse, workspace)
+        _check("mla_decode_fwd_splits", load_library().mla_decode_fwd_splits(*args))
+    return out, lse, workspace
+
+
+def mla_combine_splits(num_splits, s_q: int, h_q: int, num_units: int, out, lse, workspace):
+    """Second stage of mla_decode_fwd only (the split combine kernel)."""
+    import torch
+    _need(num_splits, torch.int32, "num_splits")
+    B = int(num_splits.shape[0]) - 1
+    with torch.cuda.device(num_splits.device):
+        _check("mla_combine_splits", load_library().mla_combine_splits(
+            num_splits.data_ptr(), B, s_q, h_q, num_units, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+            int(workspace.numel()), _stream(torch)))
     return out, lse
 
 
@@ -181,5 +216,6 @@ def workspace_bytes(batch: int, s_q: int, h_q: int, num_units: int) -> int:
 
 
 __all__ = ["mla_plan_sizes", "mla_workspace_bytes", "mla_get_metadata", "mla_get_metadata_host", "mla_decode_fwd",
+           "mla_decode_fwd_splits", "mla_combine_splits",
            "workspace_bytes", "load_library", "status_string", "MLAError", "LIB_PATH",
            "D_QK", "D_V", "PAGE_SIZE", "META_INTS"]

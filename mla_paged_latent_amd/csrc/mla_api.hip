@@ -7,8 +7,8 @@
 #include "mla_common.h"
 
 namespace mla {
-void plan_host(const int32_t* seqlens, int batch, int kappa, int num_units, int32_t* meta, int32_t* splits);
-hipError_t launch_plan(const int32_t* seqlens, int batch, int kappa, int num_units, int32_t* meta,
+void plan_host(const int32_t* seqlens, int batch, int rows_wg, int num_units, int32_t* meta, int32_t* splits);
+hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_units, int32_t* meta,
                        int32_t* splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
@@ -30,7 +30,8 @@ int check_shape(int batch, int s_q, int h_q)
 }
 
 struct Geometry {
-    int rows_total, rows_wg, head_groups, kappa;
+    int rows_total, rows_wg, head_groups;
+    bool by_sequence;
 };
 
 Geometry geometry(int s_q, int h_q)
@@ -39,8 +40,16 @@ Geometry geometry(int s_q, int h_q)
     g.rows_total = s_q * h_q;
     g.rows_wg = mla::rows_per_wg(g.rows_total);
     g.head_groups = g.rows_total / g.rows_wg;
-    g.kappa = mla::segment_cost(g.rows_wg);
+    g.by_sequence = mla::plan_by_sequence(g.rows_wg);
     return g;
+}
+
+// Per-sequence plans need at least one unit per sequence plus one to spread.
+int check_units(const Geometry& geo, int batch, int num_units)
+{
+    if (num_units < 1) return MLA_ERR_INVALID_ARG;
+    if (geo.by_sequence && num_units < batch + 1) return MLA_ERR_INVALID_ARG;
+    return MLA_OK;
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -83,9 +92,11 @@ int mla_plan_sizes(int batch, int s_q, int h_q, int num_cus, int* num_units, siz
         if (num_cus <= 0) return MLA_ERR_HIP;
     }
     const Geometry geo = geometry(s_q, h_q);
-    // one workgroup per CU (the block buffers fill most of the LDS)
+    // one workgroup per CU (the block buffers fill most of the LDS); a
+    // per-sequence plan adds one unit per sequence for the rounding of splits
     int units = num_cus / geo.head_groups;
     if (units < 1) units = 1;
+    if (geo.by_sequence) units += batch;
     size_t part_o = 0, total = 0;
     workspace_layout(batch, geo.rows_total, units, &part_o, &total);
     if (num_units) *num_units = units;
@@ -99,7 +110,7 @@ int mla_workspace_bytes(int batch, int s_q, int h_q, int num_units, size_t* work
 {
     int rc = check_shape(batch, s_q, h_q);
     if (rc != MLA_OK) return rc;
-    if (num_units < 1 || !workspace_bytes) return MLA_ERR_INVALID_ARG;
+    if (!workspace_bytes || check_units(geometry(s_q, h_q), batch, num_units) != MLA_OK) return MLA_ERR_INVALID_ARG;
     size_t part_o = 0;
     workspace_layout(batch, s_q * h_q, num_units, &part_o, workspace_bytes);
     return MLA_OK;
@@ -110,9 +121,10 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, 
 {
     int rc = check_shape(batch, s_q, h_q);
     if (rc != MLA_OK) return rc;
-    if (!cache_seqlens || !tile_meta || !num_splits || num_units < 1) return MLA_ERR_INVALID_ARG;
+    if (!cache_seqlens || !tile_meta || !num_splits) return MLA_ERR_INVALID_ARG;
     const Geometry geo = geometry(s_q, h_q);
-    if (mla::launch_plan(cache_seqlens, batch, geo.kappa, num_units, tile_meta, num_splits,
+    if (check_units(geo, batch, num_units) != MLA_OK) return MLA_ERR_INVALID_ARG;
+    if (mla::launch_plan(cache_seqlens, batch, geo.rows_wg, num_units, tile_meta, num_splits,
                          (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_HIP;
     return MLA_OK;
@@ -123,11 +135,74 @@ int mla_get_metadata_host(const int32_t* cache_seqlens, int batch, int s_q, int 
 {
     int rc = check_shape(batch, s_q, h_q);
     if (rc != MLA_OK) return rc;
-    if (!cache_seqlens || !tile_meta || !num_splits || num_units < 1) return MLA_ERR_INVALID_ARG;
+    if (!cache_seqlens || !tile_meta || !num_splits) return MLA_ERR_INVALID_ARG;
     const Geometry geo = geometry(s_q, h_q);
-    mla::plan_host(cache_seqlens, batch, geo.kappa, num_units, tile_meta, num_splits);
+    if (check_units(geo, batch, num_units) != MLA_OK) return MLA_ERR_INVALID_ARG;
+    mla::plan_host(cache_seqlens, batch, geo.rows_wg, num_units, tile_meta, num_splits);
     return MLA_OK;
 }
+
+}  // extern "C"
+
+namespace {
+
+int setup_decode(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table, int max_blocks,
+                 const int32_t* cache_seqlens, int batch, int s_q, int h_q, float softmax_scale, int causal,
+                 const int32_t* tile_meta, const int32_t* num_splits, int num_units, void* out, float* lse,
+                 void* workspace, size_t workspace_bytes, mla::DecodeParams* p, Geometry* geo_out)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (!q || !kcache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse ||
+        !workspace)
+        return MLA_ERR_INVALID_ARG;
+    if (nblocks < 1 || max_blocks < 1 || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(out) || !aligned16(workspace) || ((uintptr_t)lse & 3u))
+        return MLA_ERR_INVALID_ARG;
+    const Geometry geo = geometry(s_q, h_q);
+    if (check_units(geo, batch, num_units) != MLA_OK) return MLA_ERR_INVALID_ARG;
+    size_t part_o = 0, total = 0;
+    workspace_layout(batch, geo.rows_total, num_units, &part_o, &total);
+    if (workspace_bytes < total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    p->q = (const uint16_t*)q;
+    p->kcache = (const uint16_t*)kcache;
+    p->block_table = block_table;
+    p->seqlens = cache_seqlens;
+    p->meta = tile_meta;
+    p->splits = num_splits;
+    p->out = (uint16_t*)out;
+    p->lse = lse;
+    p->part_o = (float*)workspace;
+    p->part_lse = (float*)((char*)workspace + part_o);
+    p->nblocks = nblocks;
+    p->max_blocks = max_blocks;
+    p->batch = batch;
+    p->s_q = s_q;
+    p->h_q = h_q;
+    p->rows_total = geo.rows_total;
+    p->causal = causal ? 1 : 0;
+    p->scale_log2 = softmax_scale * 1.4426950408889634f;
+    *geo_out = geo;
+    return MLA_OK;
+}
+
+int run_combine(const mla::DecodeParams& p, hipStream_t st)
+{
+    mla::CombineParams c;
+    c.splits = p.splits;
+    c.part_o = p.part_o;
+    c.part_lse = p.part_lse;
+    c.out = p.out;
+    c.lse = p.lse;
+    c.batch = p.batch;
+    c.rows_total = p.rows_total;
+    return mla::launch_combine(c, st) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
 
 int mla_decode_fwd(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table,
                    int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q,
@@ -135,52 +210,55 @@ int mla_decode_fwd(const void* q, const void* kcache, int64_t nblocks, const int
                    int num_units, void* out, float* lse, void* workspace, size_t workspace_bytes,
                    void* stream)
 {
+    mla::DecodeParams p;
+    Geometry geo;
+    int rc = setup_decode(q, kcache, nblocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                          softmax_scale, causal, tile_meta, num_splits, num_units, out, lse, workspace,
+                          workspace_bytes, &p, &geo);
+    if (rc != MLA_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (mla::launch_decode(p, num_units, geo.head_groups, geo.rows_wg, st) != hipSuccess) return MLA_ERR_HIP;
+    return run_combine(p, st);
+}
+
+int mla_decode_fwd_splits(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table,
+                          int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                          float softmax_scale, int causal, const int32_t* tile_meta, const int32_t* num_splits,
+                          int num_units, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream)
+{
+    mla::DecodeParams p;
+    Geometry geo;
+    int rc = setup_decode(q, kcache, nblocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                          softmax_scale, causal, tile_meta, num_splits, num_units, out, lse, workspace,
+                          workspace_bytes, &p, &geo);
+    if (rc != MLA_OK) return rc;
+    if (mla::launch_decode(p, num_units, geo.head_groups, geo.rows_wg, (hipStream_t)stream) != hipSuccess)
+        return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, int num_units, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
     int rc = check_shape(batch, s_q, h_q);
     if (rc != MLA_OK) return rc;
-    if (!q || !kcache || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse ||
-        !workspace)
-        return MLA_ERR_INVALID_ARG;
-    if (nblocks < 1 || max_blocks < 1 || num_units < 1 || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(kcache) || !aligned16(out) || !aligned16(workspace) || ((uintptr_t)lse & 3u))
-        return MLA_ERR_INVALID_ARG;
+    if (!num_splits || !out || !lse || !workspace) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(out) || !aligned16(workspace) || ((uintptr_t)lse & 3u)) return MLA_ERR_INVALID_ARG;
     const Geometry geo = geometry(s_q, h_q);
+    if (check_units(geo, batch, num_units) != MLA_OK) return MLA_ERR_INVALID_ARG;
     size_t part_o = 0, total = 0;
     workspace_layout(batch, geo.rows_total, num_units, &part_o, &total);
     if (workspace_bytes < total) return MLA_ERR_WORKSPACE_TOO_SMALL;
-
     mla::DecodeParams p;
-    p.q = (const uint16_t*)q;
-    p.kcache = (const uint16_t*)kcache;
-    p.block_table = block_table;
-    p.seqlens = cache_seqlens;
-    p.meta = tile_meta;
     p.splits = num_splits;
-    p.out = (uint16_t*)out;
-    p.lse = lse;
     p.part_o = (float*)workspace;
     p.part_lse = (float*)((char*)workspace + part_o);
-    p.nblocks = nblocks;
-    p.max_blocks = max_blocks;
+    p.out = (uint16_t*)out;
+    p.lse = lse;
     p.batch = batch;
-    p.s_q = s_q;
-    p.h_q = h_q;
     p.rows_total = geo.rows_total;
-    p.causal = causal ? 1 : 0;
-    p.scale_log2 = softmax_scale * 1.4426950408889634f;
-
-    hipStream_t st = (hipStream_t)stream;
-    if (mla::launch_decode(p, num_units, geo.head_groups, geo.rows_wg, st) != hipSuccess) return MLA_ERR_HIP;
-
-    mla::CombineParams c;
-    c.splits = num_splits;
-    c.part_o = p.part_o;
-    c.part_lse = p.part_lse;
-    c.out = p.out;
-    c.lse = lse;
-    c.batch = batch;
-    c.rows_total = geo.rows_total;
-    if (mla::launch_combine(c, st) != hipSuccess) return MLA_ERR_HIP;
-    return MLA_OK;
+    return run_combine(p, (hipStream_t)stream);
 }
 
 }  // extern "C"

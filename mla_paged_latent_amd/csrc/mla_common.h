@@ -1,5 +1,5 @@
-// Shared definitions of the HIP library: launch shapes, the split-KV plan's
-// integer formulas (used by both the device planner and the host planner so
+// Shared definitions of the HIP library: shapes, launch geometry, the split-KV
+// plan's integer formulas (used by the device planner and the host planner so
 // the two agree bit for bit) and the kernel parameter blocks.
 #pragma once
 
@@ -16,40 +16,47 @@ constexpr int kPageBytes = kPage * kRowBytes;   // 73,728 B, contiguous in HBM
 constexpr int kMetaInts = 8;
 constexpr int kMaxRows = 1024;     // largest s_q*h_q accepted
 
-// Query rows per workgroup: the largest of 128/64/32/16 dividing s_q*h_q.
-// Rows beyond that are covered by more workgroups ("head groups") that read
-// the same cache blocks.
+// Query rows per workgroup: 128 when s_q*h_q is a multiple of 128 (the
+// 32x32-MFMA kernel, four waves of 32 rows), else 16 (the streaming kernel,
+// every wave holds all 16 rows). Rows beyond that are covered by more
+// workgroups ("head groups") reading the same cache blocks.
 inline __host__ __device__ int rows_per_wg(int rows_total)
 {
-    if (rows_total % 128 == 0) return 128;
-    if (rows_total % 64 == 0) return 64;
-    if (rows_total % 32 == 0) return 32;
-    return 16;
+    return rows_total % 128 == 0 ? 128 : 16;
 }
 
-// Fixed cost of one (unit, sequence) segment, in cache blocks: loading the
-// queries and writing a partial result costs about this much traffic.
-inline __host__ __device__ int segment_cost(int rows_wg) { return 1 + rows_wg / 32; }
+// Two plan shapes.
+//  * Streaming kernel (16 rows): every unit is one sequence's run of blocks.
+//    W = ceil(total_blocks / G) blocks at most per unit; sequence b is cut into
+//    ns_b = ceil(n_b / W) near-equal runs. Units number sum(ns_b) <= G + B.
+//  * 128-row kernel: blocks of the batch, in (sequence, block) order, sit on a
+//    cost line where sequence b starts at P[b] and pays a fixed segment cost
+//    kappa before its first block; unit u owns the blocks whose position lies
+//    in [u*W, (u+1)*W), W = ceil(C / G). A unit may span several sequences.
+inline __host__ __device__ bool plan_by_sequence(int rows_wg) { return rows_wg < 128; }
+
+// Fixed cost of one (unit, sequence) segment of the 128-row kernel, in cache
+// blocks: reloading 128 query rows and writing 128 result rows costs about
+// this much traffic.
+constexpr int kSegmentCost = 4;
 
 inline __host__ __device__ int blocks_of(int len) { return len > 0 ? (len + kPage - 1) / kPage : 0; }
 
-// Plan geometry: the blocks of the batch, in (sequence, block) order, sit on a
-// "cost line". Sequence b starts at P[b] (exclusive prefix sum of cost_b =
-// n_b + kappa for non-empty sequences, 0 otherwise); its block j sits at
-// P[b] + kappa + j. Unit u owns the blocks whose position lies in
-// [u*W, (u+1)*W), W = ceil(C / G) with C = P[batch].
+inline __host__ __device__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
 inline __host__ __device__ int plan_width(int total_cost, int num_units)
 {
-    int w = (total_cost + num_units - 1) / num_units;
+    int w = ceil_div(total_cost, num_units);
     return w > 0 ? w : 1;
 }
 
-// First block (b, j) whose position is >= T. P has batch+1 entries.
-// Returns b = batch, j = 0 when no block qualifies.
+// Cost-line plan: first block (b, j) whose position is >= T. P has batch+1
+// entries. Returns b = batch, j = 0 when no block qualifies.
 inline __host__ __device__ void plan_locate(const int* P, int batch, int kappa, int T, int* b_out, int* j_out)
 {
-    // smallest b with P[b+1] > T (such a b always has blocks: see plan notes)
-    int lo = 0, hi = batch;                     // answer in [lo, hi]
+    // smallest b with P[b+1] > T; such a b always has blocks (an empty sequence
+    // has P[b+1] == P[b], so an earlier b would already qualify)
+    int lo = 0, hi = batch;
     while (lo < hi) {
         int mid = (lo + hi) >> 1;
         if (P[mid + 1] > T) hi = mid; else lo = mid + 1;
@@ -60,11 +67,28 @@ inline __host__ __device__ void plan_locate(const int* P, int batch, int kappa, 
     *j_out = j > 0 ? j : 0;
 }
 
-// Units touching sequence b (0 when it has no block).
+// Cost-line plan: units touching sequence b (0 when it has no block).
 inline __host__ __device__ int plan_splits(int Pb, int nb, int kappa, int W)
 {
     if (nb <= 0) return 0;
     return (Pb + kappa + nb - 1) / W - (Pb + kappa) / W + 1;
+}
+
+// Per-sequence plan: sequence b's split k covers blocks [k*n/ns, (k+1)*n/ns).
+inline __host__ __device__ int split_begin(int n, int ns, int k) { return (int)(((long long)k * n) / ns); }
+
+// Per-sequence plan: unit u -> (sequence, split) given prefix sums Q of the
+// split counts (Q[0] = 0, Q[batch] = total units). Returns b = batch if u is
+// past the last unit.
+inline __host__ __device__ int plan_owner(const int* Q, int batch, int u)
+{
+    // largest b with Q[b] <= u and Q[b+1] > u
+    int lo = 0, hi = batch;
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (Q[mid + 1] > u) hi = mid; else lo = mid + 1;
+    }
+    return lo;
 }
 
 struct DecodeParams {

@@ -1,44 +1,47 @@
-// MLA decode kernel for gfx950 (CDNA4): paged latent cache -> LDS -> bf16 MFMA.
-//
-// What one workgroup does (unit u of the split-KV plan, head group hg):
-//   for each segment (sequence b, blocks [j0, j1)) of its unit:
-//     load its 16*NR query rows into VGPRs (MFMA B-operand layout);
-//     for each cache block (64 tokens x 576 bf16 = 73,728 contiguous bytes):
-//       copy the block into one of two LDS buffers with direct global->LDS
-//       loads (the next block is in flight while this one is used), zeroing
-//       rows past the sequence end so that they contribute exactly 0;
-//       S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows from LDS);
-//       scale, causal/length mask, online softmax in fp32 (exp2 domain);
-//       O^T += V^T P^T on MFMA, V = first 512 columns of the same LDS rows,
-//       P taken straight from the S^T accumulators (no LDS round trip);
-//     merge the NK waves that split the tokens, then write out/lse, or a
-//     normalised fp32 partial and its lse when the sequence is split.
+// MLA decode kernels for gfx950 (CDNA4): paged latent cache -> LDS -> bf16 MFMA.
 //
 // The method: decode-time attention of new queries over cached rows
 // ("OpenSourceWeek Day 1: FlashMLA", bibleofai.com, "How KV Caching Works?")
-// with one latent row shared by all heads (same page, "How MLA Optimizes
-// Memory Usage?"), scaled dot-product softmax (FlashMLA explainer,
-// theflyingbirds.in, section 4.1.1), 64-token pages (same explainer, 4.3.2),
-// blocks staged on chip before use and read with contiguous accesses
-// (explainer 4.2.1-4.2.2), softmax fused with the matrix products (4.2.3).
+// with one latent row per token shared by all heads (same page, "How MLA
+// Optimizes Memory Usage?"), scaled dot-product softmax (FlashMLA explainer,
+// theflyingbirds.in, section 4.1.1), 64-token pages behind a block table
+// (explainer 4.3.2; bibleofai "Key Highlights"), blocks staged on chip and
+// read with contiguous accesses (explainer 4.2.1-4.2.2), softmax fused with
+// the two matrix products (explainer 4.2.3).
 //
-// Wave roles: NR row groups x NK token slices. Wave (rg, kk) owns query rows
-// [16 rg, 16 rg + 16) of the workgroup and tokens [kk*64/NK, (kk+1)*64/NK) of
-// every block; each wave keeps its own running max/sum/O and the NK slices are
-// merged once per segment.
+// Two decode kernels share the data path below; they differ in how the four
+// waves of a workgroup divide the work.
 //
-// Register layouts (v_mfma_f32_16x16x32_bf16: lane l, group g = l/16):
-//   A operand: row (l%16), k = 8g..8g+7; B operand: column (l%16), same k;
-//   D: column (l%16), rows 4g..4g+3.
-//   S^T tile (tokens x rows): lane holds row (l%16), tokens 4g..4g+3 of a
-//   16-token sub-tile -- exactly the P^T B-operand of the PV product when the
-//   k index of element e is token 4g+e (sub-tile st0) or 4g+e-4 (st1).
-//   O^T (512 dims x 16 rows): 32 tiles, lane holds row (l%16), dims 16nt+4g+i.
+//  * Streaming kernel (16 query rows per workgroup): every wave holds
+//    all the workgroup's rows and streams its own 16-token sub-tiles through a
+//    private two-slot LDS ring (direct global->LDS loads, no workgroup barrier
+//    in the loop), so each CU keeps up to 8 x 18 KB of cache in flight. The
+//    four waves' partial softmax states are merged once at the end. QK^T on
+//    v_mfma_f32_16x16x32_bf16, PV on v_mfma_f32_16x16x16_bf16.
+//  * Wide kernel (128 query rows): four waves of 32 rows share a ring of four
+//    32-token LDS slots (three in flight while one is used); QK^T and PV on
+//    v_mfma_f32_32x32x16_bf16. A unit may cover several sequences.
 //
-// LDS block layout: row r (token) is 72 chunks of 16 B followed by one unused
-// 16 B pad, so the row stride is 1168 B: 8 consecutive rows reading the same
-// chunk land on 8 different 16-byte bank groups, and every operand address is
-// one per-lane base plus a compile-time offset.
+// Data path common to both:
+//  * a cache block is 64 contiguous rows of 1152 B; each LDS row is 72 chunks
+//    of 16 B plus one pad chunk (stride 1168 B);
+//  * S^T = K Q^T: K rows are the MFMA A operand (ds_read_b128), Q^T the B
+//    operand held in VGPRs. The S^T accumulator layout (lane = query row,
+//    4 tokens per element group) is exactly the P^T B operand of O^T = V^T P^T,
+//    so P never leaves registers;
+//  * V^T comes from ds_read_b64_tr_b16: within each 16-lane group, output lane
+//    j element e is element j%4 of what source lane 4e + j/4 read, so source
+//    lanes read 4 dims of 4 token rows and every output lane ends with one dim
+//    of 4 tokens -- the MFMA A operand;
+//  * the MFMA row <-> token map is permuted, token(a) = 8(a/8) + 2(a%4) + (a/4)%2,
+//    so that 8 consecutive A rows hit 8 different 16-byte bank groups and the 4
+//    rows a transpose read combines hit 4 different 32-byte bank groups;
+//  * scores are scaled into the exp2 domain; the running max is raised (and O
+//    rescaled) only when a score exceeds it by more than 2^8, so P <= 256;
+//  * rows past the end of a sequence are loaded from the block's first valid
+//    row instead (finite data, masked to p = 0), so no LDS row holds garbage;
+//  * block-table entries and scalars are read with scalar loads so that they
+//    never wait on the vector-memory counter that tracks the block copies.
 #include "mla_common.h"
 
 namespace mla {
@@ -47,364 +50,595 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) s16x8 lds_s16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
 
-constexpr int kChunks = kRowBytes / 16;          // 72 chunks of 16 B per row
-constexpr int kSlots = kChunks + 1;              // 73 LDS slots per row (one pad)
-constexpr int kLdsRow = kSlots * 16;             // 1168 B
-constexpr int kDmaInstr = (kPage * kSlots + 63) / 64;   // 73 wave-wide 1 KB loads per block
-constexpr int kBufBytes = kDmaInstr * 1024;      // 74,752 B
-constexpr int kLdsBytes = 2 * kBufBytes;         // 149,504 B
-constexpr int kObufStride = kDv + 4;             // fp32 row stride of the merge buffer
+constexpr int kLdsRow = 1168;            // LDS row stride: 72 data chunks + 1 pad chunk of 16 B
+constexpr int kRowSlots = 73;
+constexpr int kChunks = 72;
+constexpr float kLazyTau = 8.f;          // exp2-domain slack of the running max
+constexpr float kLn2 = 0.69314718055994531f;
 
-typedef __attribute__((address_space(3))) void lds_void;
+// ---------------------------------------------------------------- primitives
 
+// One 16-byte global->LDS copy per lane. lds_addr (uniform) is the LDS byte
+// address of the wave's 1 KB destination; lane l lands at lds_addr + 16 l.
+// Issued through asm so the compiler does not order later LDS reads of other
+// buffers behind it; completion is awaited explicitly with vmcnt.
+__device__ __forceinline__ void dma16(const unsigned char* gptr, unsigned lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory");
+}
 
-__device__ __forceinline__ unsigned short bf16_bits_rne(float f)
+#define MLA_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+
+// vmcnt(0) issued through the builtin, which the compiler's own wait-count
+// tracking sees: after it, loads the compiler issued (queries, table rows) are
+// known complete, so it inserts no waits for them inside the copy pipeline
+// (such a wait would also stall on every block copy in flight).
+__device__ __forceinline__ void settle_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ void wg_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Scalar load of a wave-uniform int (waits for it in the same asm block).
+__device__ __forceinline__ int sload(const int32_t* ptr)
+{
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ unsigned lds_base(unsigned char* smem)
+{
+    return (unsigned)(uintptr_t)(lds_u8*)smem;
+}
+
+__device__ __forceinline__ s16x8 lds_load16(unsigned addr) { return *(const lds_s16x8*)(uintptr_t)addr; }
+
+__device__ __forceinline__ s16x4 lds_tr4(unsigned addr)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
+}
+
+__device__ __forceinline__ int token_of_row(int a) { return ((a >> 3) << 3) + ((a & 3) << 1) + ((a >> 2) & 1); }
+
+__device__ __forceinline__ unsigned short bf16_rne(float f)
 {
     unsigned u = __float_as_uint(f);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (unsigned short)(u >> 16);
 }
 
-// Issue the direct-to-LDS copy of one cache block. Rows >= valid are not read.
-// Wave w issues 1 KB loads w, w+NW, ...; lane l of load i fills LDS bytes
-// [1024 i + 16 l, +16), which is slot s of row r with 73 r + s = 64 i + l
-// (slot 72 is the pad and is not loaded).
-template <int NW>
-__device__ __forceinline__ void issue_block(unsigned char* buf, const unsigned char* src, int valid, int wave, int lane)
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+// Copy rows [0, 16 or 32) of a block run starting at gbase (valid of them real)
+// into an LDS slot; copies first, first+step, ... < ninstr of 1 KB each.
+__device__ __forceinline__ void copy_rows(const unsigned char* gbase, int valid, unsigned slot, int first,
+                                          int step, int ninstr, int lane)
 {
-#pragma unroll 1
-    for (int i = wave; i < kDmaInstr; i += NW) {
+    for (int i = first; i < ninstr; i += step) {
         const int q = i * 64 + lane;
-        const int r = q / kSlots;
-        const int s = q - r * kSlots;
-        if (r < valid && s < kChunks) {
-            __builtin_amdgcn_global_load_lds((const void*)(src + r * kRowBytes + s * 16),
-                                             (lds_void*)(buf + i * 1024), 16, 0, 0);
-        }
+        int r = q / kRowSlots;
+        int c = q - r * kRowSlots;
+        r = r < valid ? r : 0;
+        c = c < kChunks ? c : 0;
+        dma16(gbase + r * kRowBytes + c * 16, slot + (unsigned)i * 1024u);
     }
 }
 
-template <int NT>
-__device__ __forceinline__ void zero_rows(unsigned char* buf, int first_row)
+// ---------------------------------------------------------------- streaming kernel
+
+constexpr int kSlotA = 19 * 1024;        // 16 rows x 1168 B, rounded up to whole 1 KB copies
+constexpr int kDmaA = 19;
+constexpr int kLdsA = 8 * kSlotA;        // two slots per wave: 155,648 B
+constexpr int kObufA = 16 * 516 * 4;     // one wave's 16 x 512 fp32 (row stride 516) merge region
+
+template <int NR>
+__global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
 {
-    const int n = (kPage - first_row) * kChunks;
-    for (int k = threadIdx.x; k < n; k += NT) {
-        const int r = first_row + k / kChunks;
-        const int s = k % kChunks;
-        *(uint4*)(buf + r * kLdsRow + s * 16) = make_uint4(0, 0, 0, 0);
-    }
-}
-
-template <int NR, int NK>
-__global__ __launch_bounds__(64 * NR * NK) void decode_kernel(DecodeParams p)
-{
-    constexpr int NW = NR * NK;
-    constexpr int NT = 64 * NW;
-    constexpr int MW = 16 * NR;          // query rows per workgroup
-    constexpr int TW = kPage / NK;       // tokens per wave per block
-    constexpr int NST = TW / 16;         // 16-token sub-tiles per wave per block
-    static_assert(NST >= 1, "token slice too small");
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int rg = wave % NR;
-    const int kk = wave / NR;
+    constexpr int R = 16 * NR;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsA];
+    const unsigned lds0 = lds_base(smem);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int c16 = lane & 15;
 
     const int32_t* meta = p.meta + (size_t)blockIdx.x * kMetaInts;
-    const int b_end = meta[2];
-    const int j_end = meta[3];
-    int b = meta[0];
-    int jb = meta[1];
-    int split = meta[4];
+    const int b = sload(meta + 0);
+    const int j0 = sload(meta + 1);
+    const int j1 = sload(meta + 3);
+    const int split = sload(meta + 4);
+    if (b >= p.batch || j0 >= j1) return;
+    const int L = sload(p.seqlens + b);
+    const int tok_begin = j0 * kPage;
+    const int tok_end = min(j1 * kPage, L);
+    const int nsub = (tok_end - tok_begin + 15) >> 4;
+    const int K = nsub > wave ? (nsub - wave + 3) >> 2 : 0;   // this wave's sub-tiles: wave, wave+4, ...
+    const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
+    const int npages = j1 - j0;
+    const int page_vec = lane < npages ? table[j0 + lane] : 0;
 
-    const int row_wave = blockIdx.y * MW + rg * 16;      // first row of this wave's tile
-    const int myrow = row_wave + c16;                    // the row this lane's stats belong to
-    const int iq = myrow / p.h_q;                        // new-token index of that row
-
-    for (; b <= b_end && b < p.batch; ++b, jb = 0, split = 0) {
-        const int L = p.seqlens[b];
-        const int nb = blocks_of(L);
-        const int je = (b == b_end) ? j_end : nb;
-        if (jb >= je) continue;
-        const int lim = p.causal ? L - (p.s_q - 1 - iq) : L;   // tokens t < lim are visible to myrow
-        const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
-
-        // queries: lane holds row myrow, columns 8g + 32ks .. +8
-        bf16x8 qf[18];
-        {
-            const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + myrow) * kDqk + 8 * g;
+    bf16x8 qf[NR][18];
+    int lim[NR];
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks)
-                qf[ks] = __builtin_bit_cast(bf16x8, *(const s16x8*)(qrow + 32 * ks));
+    for (int rt = 0; rt < NR; ++rt) {
+        const int row = blockIdx.y * R + rt * 16 + c16;
+        const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + row) * kDqk + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, *(const s16x8*)(qrow + 32 * ks));
+        const int iq = row / p.h_q;
+        lim[rt] = min(tok_end, p.causal ? L - (p.s_q - 1 - iq) : L);
+    }
+    settle_loads();
+
+    float mrun[NR], lrun[NR];
+    f32x4 acc[NR][32];
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+        mrun[rt] = -INFINITY;
+        lrun[rt] = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) acc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const unsigned slot0 = lds0 + (unsigned)(2 * wave) * kSlotA;
+    auto issue = [&](int k) {
+        const int tok = tok_begin + 16 * (wave + 4 * k);
+        const int pidx = (tok >> 6) - j0;
+        const int page = pidx < 64 ? __builtin_amdgcn_readlane(page_vec, pidx) : sload(table + j0 + pidx);
+        const unsigned char* gbase = (const unsigned char*)p.kcache + (size_t)page * kPageBytes +
+                                     (size_t)(tok & 63) * kRowBytes;
+        copy_rows(gbase, min(16, tok_end - tok), slot0 + (unsigned)(k & 1) * kSlotA, 0, 1, kDmaA, lane);
+    };
+
+    if (K > 0) issue(0);
+    if (K > 1) issue(1);
+
+    const unsigned a_off = (unsigned)(token_of_row(c16) * kLdsRow + g * 16);
+    const unsigned v_off = (unsigned)(token_of_row(4 * g + (c16 >> 2)) * kLdsRow + 8 * (c16 & 3));
+    for (int k = 0; k < K; ++k) {
+        if (k + 1 < K) MLA_WAIT_VM(19); else MLA_WAIT_VM(0);
+        const unsigned sb = slot0 + (unsigned)(k & 1) * kSlotA;
+        const int tok0 = tok_begin + 16 * (wave + 4 * k);
+
+        // S^T = K Q^T for 16 tokens x R rows
+        f32x4 s[NR];
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) s[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(sb + a_off + 64 * ks));
+#pragma unroll
+            for (int rt = 0; rt < NR; ++rt) s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][ks], s[rt], 0, 0, 0);
         }
-        float mrow = -INFINITY;
-        float lrow = 0.f;
-        f32x4 acc[32];
-#pragma unroll
-        for (int nt = 0; nt < 32; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        {
-            const unsigned char* src = (const unsigned char*)p.kcache + (size_t)table[jb] * kPageBytes;
-            issue_block<NW>(smem, src, min(kPage, L - jb * kPage), wave, lane);
-        }
-        for (int j = jb; j < je; ++j) {
-            unsigned char* buf = smem + ((j - jb) & 1) * kBufBytes;
-            const int valid = min(kPage, L - j * kPage);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (valid < kPage) zero_rows<NT>(buf, valid);
-            __syncthreads();
-            if (j + 1 < je) {
-                const unsigned char* src = (const unsigned char*)p.kcache + (size_t)table[j + 1] * kPageBytes;
-                issue_block<NW>(smem + ((j + 1 - jb) & 1) * kBufBytes, src,
-                                min(kPage, L - (j + 1) * kPage), wave, lane);
-            }
-
-            // ---- S^T = K Q^T over this wave's tokens
-            const int tok0 = kk * TW;
-            f32x4 s[NST];
+        // scale, mask, online softmax; s[rt][i] is token tok0 + token_of_row(4g + i)
+        s16x4 pb[NR];
 #pragma unroll
-            for (int st = 0; st < NST; ++st) {
-                s[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int r = tok0 + 16 * st + c16;
-#pragma unroll
-                for (int ks = 0; ks < 18; ++ks) {
-                    const s16x8 a = *(const s16x8*)(buf + r * kLdsRow + (g + 4 * ks) * 16);
-                    s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[st], 0, 0, 0);
-                    if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-
-            // ---- scale, mask, online softmax (log2 domain)
+        for (int rt = 0; rt < NR; ++rt) {
             float tmax = -INFINITY;
 #pragma unroll
-            for (int st = 0; st < NST; ++st) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = j * kPage + tok0 + 16 * st + 4 * g + i;
-                    const float v = (t < lim) ? s[st][i] * p.scale_log2 : -INFINITY;
-                    s[st][i] = v;
-                    tmax = fmaxf(tmax, v);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int t = tok0 + token_of_row(4 * g + i);
+                const float v = (t < lim[rt]) ? s[rt][i] * p.scale_log2 : -INFINITY;
+                s[rt][i] = v;
+                tmax = fmaxf(tmax, v);
             }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float mnew = fmaxf(mrow, tmax);
-            const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = exp2f(mrow - muse);
+            const bool need = tmax > mrun[rt] + kLazyTau;
+            if (wave_any(need)) {
+                const float mnew = need ? tmax : mrun[rt];
+                const float alpha = need ? exp2f(mrun[rt] - mnew) : 1.f;
+                lrun[rt] *= alpha;
+#pragma unroll
+                for (int nt = 0; nt < 32; ++nt) acc[rt][nt] *= alpha;
+                mrun[rt] = mnew;
+            }
+            const float muse = mrun[rt] == -INFINITY ? 0.f : mrun[rt];
             float psum = 0.f;
 #pragma unroll
-            for (int st = 0; st < NST; ++st) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pv = exp2f(s[st][i] - muse);
-                    s[st][i] = pv;
-                    psum += pv;
-                }
+            for (int i = 0; i < 4; ++i) {
+                const float pv = exp2f(s[rt][i] - muse);
+                psum += pv;
+                pb[rt][i] = (short)bf16_rne(pv);
             }
             psum += __shfl_xor(psum, 16);
             psum += __shfl_xor(psum, 32);
-            lrow = lrow * alpha + psum;
-            mrow = mnew;
-#pragma unroll
-            for (int nt = 0; nt < 32; ++nt) acc[nt] *= alpha;
+            lrun[rt] += psum;
+        }
 
-            // ---- O^T += V^T P^T
-            if constexpr (NST == 1) {
-                s16x4 pb;
+        // O^T += V^T P^T
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pb[e] = (short)bf16_bits_rne(s[0][e]);
+        for (int nt = 0; nt < 32; ++nt) {
+            const s16x4 va = lds_tr4(sb + v_off + 32 * nt);
 #pragma unroll
-                for (int nt = 0; nt < 32; ++nt) {
-                    const int d = 16 * nt + c16;
-                    s16x4 va;
+            for (int rt = 0; rt < NR; ++rt) acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][nt], 0, 0, 0);
+        }
+
+        if (k + 2 < K) issue(k + 2);
+    }
+
+    // ---- merge the four waves' (m, l, O) and write the result
+    wg_barrier();
+    lds_f32* stat_m = (lds_f32*)(uintptr_t)lds0;          // [4][R]
+    lds_f32* stat_l = stat_m + 4 * R;                       // [4][R]
+    const unsigned obuf0 = lds0 + 1024;                    // 4 regions of kObufA
+    if (g == 0) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = tok0 + 4 * g + e;
-                        va[e] = *(const short*)(buf + r * kLdsRow + 2 * d);
-                    }
-                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[nt], 0, 0, 0);
-                    if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-                }
+        for (int rt = 0; rt < NR; ++rt) stat_m[wave * R + rt * 16 + c16] = mrun[rt];
+    }
+    wg_barrier();
+    float fac[NR];
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+        float mall = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mall = fmaxf(mall, stat_m[w * R + rt * 16 + c16]);
+        fac[rt] = mrun[rt] == -INFINITY ? 0.f : exp2f(mrun[rt] - mall);
+    }
+    if (g == 0) {
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) stat_l[wave * R + rt * 16 + c16] = lrun[rt] * fac[rt];
+    }
+    const int nsplit = sload(p.splits + b + 1) - sload(p.splits + b);
+    const int slot = sload(p.splits + b) + split;
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+        const unsigned mine = obuf0 + (unsigned)wave * kObufA + (unsigned)(c16 * 2064 + 16 * g);
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) *(lds_f32x4*)(uintptr_t)(mine + 64 * nt) = acc[rt][nt] * fac[rt];
+        wg_barrier();
+        // wave w finishes dims [128 w, 128 w + 128) of the 16 rows of tile rt
+        for (int idx = lane; idx < 256; idx += 64) {
+            const int r = idx >> 4;
+            const int d = 128 * wave + 8 * (idx & 15);
+            f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+            float lt = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const unsigned src = obuf0 + (unsigned)w * kObufA + (unsigned)(r * 2064 + d * 4);
+                v0 += *(const lds_f32x4*)(uintptr_t)src;
+                v1 += *(const lds_f32x4*)(uintptr_t)(src + 16);
+                lt += stat_l[w * R + rt * 16 + r];
+            }
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const int grow = blockIdx.y * R + rt * 16 + r;
+            if (nsplit == 1) {
+                s16x8 o;
+                o[0] = bf16_rne(v0[0] * inv); o[1] = bf16_rne(v0[1] * inv);
+                o[2] = bf16_rne(v0[2] * inv); o[3] = bf16_rne(v0[3] * inv);
+                o[4] = bf16_rne(v1[0] * inv); o[5] = bf16_rne(v1[1] * inv);
+                o[6] = bf16_rne(v1[2] * inv); o[7] = bf16_rne(v1[3] * inv);
+                *(s16x8*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = o;
             } else {
-#pragma unroll
-                for (int kp = 0; kp < NST / 2; ++kp) {
-                    s16x8 pb;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pb[e] = (short)bf16_bits_rne(s[2 * kp][e]);
-                        pb[e + 4] = (short)bf16_bits_rne(s[2 * kp + 1][e]);
-                    }
-#pragma unroll
-                    for (int nt = 0; nt < 32; ++nt) {
-                        const int d = 16 * nt + c16;
-                        s16x8 va;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int r = tok0 + 16 * (2 * kp + (e >> 2)) + 4 * g + (e & 3);
-                            va[e] = *(const short*)(buf + r * kLdsRow + 2 * d);
-                        }
-                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
-                                                                          __builtin_bit_cast(bf16x8, pb), acc[nt], 0, 0, 0);
-                        if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
+                float* o = p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d;
+                *(f32x4*)o = v0 * inv;
+                *(f32x4*)(o + 4) = v1 * inv;
             }
         }
-        __syncthreads();     // every wave is done with the block buffers
+        if (wave == 0 && lane < 16) {
+            float lt = 0.f, mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                lt += stat_l[w * R + rt * 16 + lane];
+                mx = fmaxf(mx, stat_m[w * R + rt * 16 + lane]);
+            }
+            const float lse = lt > 0.f ? (mx + __log2f(lt)) * kLn2 : -INFINITY;
+            const int grow = blockIdx.y * R + rt * 16 + lane;
+            if (nsplit == 1) p.lse[(size_t)b * p.rows_total + grow] = lse;
+            else p.part_lse[(size_t)slot * p.rows_total + grow] = lse;
+        }
+        if (rt + 1 < NR) wg_barrier();
+    }
+}
 
-        // ---- merge the token slices and write the segment's result
-        const int nsplit = p.splits[b + 1] - p.splits[b];
-        const int slot = p.splits[b] + split;
-        if constexpr (NK == 1) {
-            const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
-            if (nsplit == 1) {
-                uint16_t* o = p.out + ((size_t)b * p.rows_total + myrow) * kDv + 4 * g;
+// ---------------------------------------------------------------- wide kernel
+
+constexpr int kSlotB = 37 * 1024;        // 32 rows x 1168 B, rounded up to whole 1 KB copies
+constexpr int kDmaB = 37;
+constexpr int kLdsB = 4 * kSlotB;        // 151,552 B
+
+// The run of sequence b inside a unit: tokens [tb, te) of a sequence of L tokens.
+struct Segment {
+    int b, tb, te, L;
+};
+
+__device__ __forceinline__ Segment unit_segment(const DecodeParams& p, int b, int b0, int j0, int b1, int j1)
+{
+    Segment s;
+    s.b = b;
+    s.L = sload(p.seqlens + b);
+    const int nb = blocks_of(s.L);
+    s.tb = (b == b0 ? j0 : 0) * kPage;
+    const int je = (b == b1) ? j1 : nb;
+    s.te = min(je * kPage, s.L);
+    return s;
+}
+
+// First non-empty segment of the unit at or after sequence b (b = batch when none).
+__device__ __forceinline__ Segment next_segment(const DecodeParams& p, int b, int b0, int j0, int b1, int j1)
+{
+    for (; b <= b1 && b < p.batch; ++b) {
+        Segment s = unit_segment(p, b, b0, j0, b1, j1);
+        if (s.tb < s.te) return s;
+    }
+    Segment none;
+    none.b = p.batch; none.tb = 0; none.te = 0; none.L = 0;
+    return none;
+}
+
+__global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsB];
+    const unsigned lds0 = lds_base(smem);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5;
+    const int r32 = lane & 31;
+    const int i16 = lane & 15;
+    const int dh = (lane >> 4) & 1;
+
+    const int32_t* meta = p.meta + (size_t)blockIdx.x * kMetaInts;
+    const int b0 = sload(meta + 0);
+    const int j0 = sload(meta + 1);
+    const int b1 = sload(meta + 2);
+    const int j1 = sload(meta + 3);
+    const int split0 = sload(meta + 4);
+
+    const int row = blockIdx.y * 128 + 32 * wave + r32;     // this lane's query row
+    const int iq = row / p.h_q;
+
+    Segment is = next_segment(p, b0, b0, j0, b1, j1);      // issue cursor
+    if (is.b >= p.batch) return;
+    int itok = is.tb;
+    int ipage_idx = -1, ipage = 0;
+    Segment cs = is;                                        // compute cursor
+    int ctok = cs.tb;
+
+    auto issue = [&](int n) {
+        const int pidx = itok >> 6;
+        if (pidx != ipage_idx) {
+            ipage = sload(p.block_table + (size_t)is.b * p.max_blocks + pidx);
+            ipage_idx = pidx;
+        }
+        const unsigned char* gbase = (const unsigned char*)p.kcache + (size_t)ipage * kPageBytes +
+                                     (size_t)(itok & 63) * kRowBytes;
+        copy_rows(gbase, min(32, is.te - itok), lds0 + (unsigned)(n & 3) * kSlotB, wave, 4, kDmaB, lane);
+        itok += 32;
+        if (itok >= is.te) {
+            is = next_segment(p, is.b + 1, b0, j0, b1, j1);
+            itok = is.tb;
+            ipage_idx = -1;
+        }
+    };
+
+    int n_issued = 0;
+    for (int k = 0; k < 3 && is.b < p.batch; ++k) issue(n_issued++);
+
+    const int cnt = wave == 0 ? 10 : 9;                    // this wave's copies per slot
+    const unsigned a_off = (unsigned)(token_of_row(r32) * kLdsRow + h * 16);
+    unsigned v_off[2][2];
 #pragma unroll
-                for (int nt = 0; nt < 32; ++nt) {
-                    ushort4 v;
-                    v.x = bf16_bits_rne(acc[nt][0] * inv);
-                    v.y = bf16_bits_rne(acc[nt][1] * inv);
-                    v.z = bf16_bits_rne(acc[nt][2] * inv);
-                    v.w = bf16_bits_rne(acc[nt][3] * inv);
-                    *(ushort4*)(o + 16 * nt) = v;
-                }
-            } else {
-                float* o = p.part_o + ((size_t)slot * p.rows_total + myrow) * kDv + 4 * g;
+    for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
-                for (int nt = 0; nt < 32; ++nt) {
-                    *(f32x4*)(o + 16 * nt) = acc[nt] * inv;
-                }
-            }
-            if (g == 0) {
-                const float l = lrow > 0.f ? (mrow + __log2f(lrow)) * 0.69314718055994531f : -INFINITY;
-                if (nsplit == 1) p.lse[(size_t)b * p.rows_total + myrow] = l;
-                else p.part_lse[(size_t)slot * p.rows_total + myrow] = l;
-            }
+        for (int half = 0; half < 2; ++half)
+            v_off[kp][half] = (unsigned)(token_of_row(16 * kp + 8 * half + 4 * h + (i16 >> 2)) * kLdsRow +
+                                         2 * (16 * dh + 4 * (i16 & 3)));
+
+    bf16x8 qf[36];
+    f32x16 acc[16];
+    float mrun = -INFINITY, lrun = 0.f;
+    int lim = 0;
+    bool drain = false;
+
+    for (int n = 0; cs.b < p.batch; ++n) {
+        const int later = n_issued - 1 - n;
+        if (drain || later == 0) {
+            MLA_WAIT_VM(0);
+        } else if (later == 1) {
+            if (cnt == 10) MLA_WAIT_VM(10); else MLA_WAIT_VM(9);
         } else {
-            float* stat_m = (float*)smem;                  // [NK][MW]
-            float* stat_l = stat_m + NK * MW;              // [NK][MW]
-            float* obuf = stat_l + NK * MW;                // [MW][kObufStride]
-            const int rloc = rg * 16 + c16;                // row within the workgroup
-            if (g == 0) stat_m[kk * MW + rloc] = mrow;
-            __syncthreads();
-            float mall = -INFINITY;
+            if (cnt == 10) MLA_WAIT_VM(20); else MLA_WAIT_VM(18);
+        }
+        drain = false;
+        wg_barrier();
+
+        if (ctok == cs.tb) {
+            // new segment: this wave's 32 query rows, fresh softmax state
+            const uint16_t* qrow = p.q + ((size_t)cs.b * p.rows_total + row) * kDqk + 8 * h;
 #pragma unroll
-            for (int k2 = 0; k2 < NK; ++k2) mall = fmaxf(mall, stat_m[k2 * MW + rloc]);
-            const float f = exp2f(mrow - ((mall == -INFINITY) ? 0.f : mall));
-            if (g == 0) stat_l[kk * MW + rloc] = lrow * f;
-            float* orow = obuf + rloc * kObufStride + 4 * g;
-            if (kk == 0) {
+            for (int ks = 0; ks < 36; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const s16x8*)(qrow + 16 * ks));
+            settle_loads();
+            mrun = -INFINITY;
+            lrun = 0.f;
 #pragma unroll
-                for (int nt = 0; nt < 32; ++nt) *(f32x4*)(orow + 16 * nt) = acc[nt] * f;
+            for (int nt = 0; nt < 16; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
+            lim = min(cs.te, p.causal ? cs.L - (p.s_q - 1 - iq) : cs.L);
+        }
+        // the buffer of slot n-1 is free: every wave has passed the barrier
+        if (is.b < p.batch) issue(n_issued++);
+        const unsigned sb = lds0 + (unsigned)(n & 3) * kSlotB;
+
+        // S^T = K Q^T: 32 tokens x 32 rows, two accumulators over the 36 k-steps
+        f32x16 s0, s1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < 36; ks += 2) {
+            const bf16x8 a0 = __builtin_bit_cast(bf16x8, lds_load16(sb + a_off + 32 * ks));
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, lds_load16(sb + a_off + 32 * ks + 32));
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks + 1], s1, 0, 0, 0);
+        }
+
+        // element i of the accumulator is token ctok + token_of_row(8(i/4) + 4h + i%4)
+        float sv[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = ctok + token_of_row(8 * (i >> 2) + 4 * h + (i & 3));
+            const float v = (t < lim) ? (s0[i] + s1[i]) * p.scale_log2 : -INFINITY;
+            sv[i] = v;
+            tmax = fmaxf(tmax, v);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool need = tmax > mrun + kLazyTau;
+        if (wave_any(need)) {
+            const float mnew = need ? tmax : mrun;
+            const float alpha = need ? exp2f(mrun - mnew) : 1.f;
+            lrun *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < 16; ++nt) acc[nt] *= alpha;
+            mrun = mnew;
+        }
+        const float muse = mrun == -INFINITY ? 0.f : mrun;
+        float psum = 0.f;
+        s16x8 pb[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float pv = exp2f(sv[i] - muse);
+            psum += pv;
+            pb[i >> 3][i & 7] = (short)bf16_rne(pv);
+        }
+        psum += __shfl_xor(psum, 32);
+        lrun += psum;
+
+        // O^T += V^T P^T over two 16-token k-steps
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt) {
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+                const s16x4 lo = lds_tr4(sb + v_off[kp][0] + 64 * nt);
+                const s16x4 hi = lds_tr4(sb + v_off[kp][1] + 64 * nt);
+                const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
+                                                                  __builtin_bit_cast(bf16x8, pb[kp]), acc[nt], 0, 0, 0);
             }
-            __syncthreads();
+        }
+
+        ctok += 32;
+        if (ctok >= cs.te) {
+            // end of segment: write this wave's 32 rows
+            const int nsplit = sload(p.splits + cs.b + 1) - sload(p.splits + cs.b);
+            const int slot = sload(p.splits + cs.b) + (cs.b == b0 ? split0 : 0);
+            const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+            if (nsplit == 1) {
+                uint16_t* o = p.out + ((size_t)cs.b * p.rows_total + row) * kDv + 4 * h;
 #pragma unroll
-            for (int k2 = 1; k2 < NK; ++k2) {
-                if (kk == k2) {
+                for (int nt = 0; nt < 16; ++nt)
 #pragma unroll
-                    for (int nt = 0; nt < 32; ++nt) *(f32x4*)(orow + 16 * nt) += acc[nt] * f;
-                }
-                __syncthreads();
+                    for (int j = 0; j < 4; ++j) {
+                        ushort4 v;
+                        v.x = bf16_rne(acc[nt][4 * j + 0] * inv);
+                        v.y = bf16_rne(acc[nt][4 * j + 1] * inv);
+                        v.z = bf16_rne(acc[nt][4 * j + 2] * inv);
+                        v.w = bf16_rne(acc[nt][4 * j + 3] * inv);
+                        *(ushort4*)(o + 32 * nt + 8 * j) = v;
+                    }
+            } else {
+                float* o = p.part_o + ((size_t)slot * p.rows_total + row) * kDv + 4 * h;
+#pragma unroll
+                for (int nt = 0; nt < 16; ++nt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        f32x4 v = {acc[nt][4 * j + 0] * inv, acc[nt][4 * j + 1] * inv,
+                                   acc[nt][4 * j + 2] * inv, acc[nt][4 * j + 3] * inv};
+                        *(f32x4*)(o + 32 * nt + 8 * j) = v;
+                    }
             }
-            // wave (rg, kk) finishes dims [kk*DS, (kk+1)*DS) of rows 16rg..16rg+15
-            constexpr int DS = kDv / NK;
-            constexpr int PER_ROW = DS / 8;
-            for (int idx = lane; idx < 16 * PER_ROW; idx += 64) {
-                const int r = rg * 16 + idx / PER_ROW;
-                const int d = kk * DS + (idx % PER_ROW) * 8;
-                float lt = 0.f;
-#pragma unroll
-                for (int k2 = 0; k2 < NK; ++k2) lt += stat_l[k2 * MW + r];
-                const float inv = lt > 0.f ? 1.f / lt : 0.f;
-                const f32x4 v0 = *(const f32x4*)(obuf + r * kObufStride + d) * inv;
-                const f32x4 v1 = *(const f32x4*)(obuf + r * kObufStride + d + 4) * inv;
-                const int grow = blockIdx.y * MW + r;
-                if (nsplit == 1) {
-                    s16x8 w;
-                    w[0] = bf16_bits_rne(v0[0]); w[1] = bf16_bits_rne(v0[1]);
-                    w[2] = bf16_bits_rne(v0[2]); w[3] = bf16_bits_rne(v0[3]);
-                    w[4] = bf16_bits_rne(v1[0]); w[5] = bf16_bits_rne(v1[1]);
-                    w[6] = bf16_bits_rne(v1[2]); w[7] = bf16_bits_rne(v1[3]);
-                    *(s16x8*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = w;
-                } else {
-                    float* o = p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d;
-                    *(f32x4*)o = v0;
-                    *(f32x4*)(o + 4) = v1;
-                }
+            if (h == 0) {
+                const float lse = lrun > 0.f ? (mrun + __log2f(lrun)) * kLn2 : -INFINITY;
+                if (nsplit == 1) p.lse[(size_t)cs.b * p.rows_total + row] = lse;
+                else p.part_lse[(size_t)slot * p.rows_total + row] = lse;
             }
-            if (kk == 0 && lane < 16) {
-                const int r = rg * 16 + lane;
-                float lt = 0.f, mx = -INFINITY;
-#pragma unroll
-                for (int k2 = 0; k2 < NK; ++k2) {
-                    lt += stat_l[k2 * MW + r];
-                    mx = fmaxf(mx, stat_m[k2 * MW + r]);
-                }
-                const float l = lt > 0.f ? (mx + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-                const int grow = blockIdx.y * MW + r;
-                if (nsplit == 1) p.lse[(size_t)b * p.rows_total + grow] = l;
-                else p.part_lse[(size_t)slot * p.rows_total + grow] = l;
-            }
-            __syncthreads();   // the merge buffer is the next segment's block buffer
+            drain = true;
+            cs = next_segment(p, cs.b + 1, b0, j0, b1, j1);
+            ctok = cs.tb;
         }
     }
 }
 
-// Merge split partials by their log-sum-exp; one wave per (sequence, row).
-// Sequences with no block get out = 0, lse = -inf; unsplit ones were written
-// by the decode kernel.
+// ---------------------------------------------------------------- split combine
+
+// Merge split partials by their log-sum-exp: out = sum_k exp(lse_k - L) o_k,
+// lse = L = log sum_k exp(lse_k). One thread per 4 dims of one (sequence, row);
+// sequences with no block get out = 0, lse = -inf; unsplit ones were written by
+// the decode kernel.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
 {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = threadIdx.x & 127;                        // 4-dim chunk of the row
+    const int row = blockIdx.x * 2 + (threadIdx.x >> 7);
     const int b = blockIdx.y;
     if (row >= p.rows_total) return;
     const int s0 = p.splits[b];
     const int ns = p.splits[b + 1] - s0;
     if (ns == 1) return;
-    uint16_t* o = p.out + ((size_t)b * p.rows_total + row) * kDv + lane * 8;
+    uint16_t* o = p.out + ((size_t)b * p.rows_total + row) * kDv + 4 * t;
     float* lo = p.lse + (size_t)b * p.rows_total + row;
     float mx = -INFINITY;
     for (int k = 0; k < ns; ++k) mx = fmaxf(mx, p.part_lse[(size_t)(s0 + k) * p.rows_total + row]);
     if (ns == 0 || mx == -INFINITY) {
-        *(uint4*)o = make_uint4(0, 0, 0, 0);
-        if (lane == 0) *lo = -INFINITY;
+        *(ushort4*)o = make_ushort4(0, 0, 0, 0);
+        if (t == 0) *lo = -INFINITY;
         return;
     }
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    for (int k = 0; k < ns; ++k) {
+    int k = 0;
+    for (; k + 4 <= ns; k += 4) {
+        f32x4 v[4];
+        float w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const size_t sr = (size_t)(s0 + k + u) * p.rows_total + row;
+            w[u] = p.part_lse[sr];
+            v[u] = *(const f32x4*)(p.part_o + sr * kDv + 4 * t);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float e = __expf(w[u] - mx);
+            wsum += e;
+            a += v[u] * e;
+        }
+    }
+    for (; k < ns; ++k) {
         const size_t sr = (size_t)(s0 + k) * p.rows_total + row;
-        const float w = __expf(p.part_lse[sr] - mx);
-        wsum += w;
-        const float* src = p.part_o + sr * kDv + lane * 8;
-        a0 += *(const f32x4*)src * w;
-        a1 += *(const f32x4*)(src + 4) * w;
+        const float e = __expf(p.part_lse[sr] - mx);
+        wsum += e;
+        a += *(const f32x4*)(p.part_o + sr * kDv + 4 * t) * e;
     }
     const float inv = 1.f / wsum;
-    s16x8 w8;
-    w8[0] = bf16_bits_rne(a0[0] * inv); w8[1] = bf16_bits_rne(a0[1] * inv);
-    w8[2] = bf16_bits_rne(a0[2] * inv); w8[3] = bf16_bits_rne(a0[3] * inv);
-    w8[4] = bf16_bits_rne(a1[0] * inv); w8[5] = bf16_bits_rne(a1[1] * inv);
-    w8[6] = bf16_bits_rne(a1[2] * inv); w8[7] = bf16_bits_rne(a1[3] * inv);
-    *(s16x8*)o = w8;
-    if (lane == 0) *lo = mx + __logf(wsum);
+    ushort4 r;
+    r.x = bf16_rne(a[0] * inv);
+    r.y = bf16_rne(a[1] * inv);
+    r.z = bf16_rne(a[2] * inv);
+    r.w = bf16_rne(a[3] * inv);
+    *(ushort4*)o = r;
+    if (t == 0) *lo = mx + __logf(wsum);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream)
 {
     dim3 grid(num_units, head_groups);
     switch (rows_wg) {
-    case 16: hipLaunchKernelGGL((decode_kernel<1, 4>), grid, dim3(256), 0, stream, p); break;
-    case 32: hipLaunchKernelGGL((decode_kernel<2, 4>), grid, dim3(512), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((decode_kernel<4, 2>), grid, dim3(512), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((decode_kernel<8, 1>), grid, dim3(512), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((decode_stream_kernel<1>), grid, dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(decode_wide_kernel, grid, dim3(256), 0, stream, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -412,7 +646,7 @@ hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, 
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream)
 {
-    dim3 grid((p.rows_total + 3) / 4, p.batch);
+    dim3 grid((p.rows_total + 1) / 2, p.batch);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }

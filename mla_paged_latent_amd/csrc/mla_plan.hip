@@ -2,16 +2,14 @@
 //
 // The pages state only that the decode kernel is tuned for serving sequences
 // of varying length (GeekNews release note, id.news.hada.io; FlashMLA
-// explainer section 2.4 on padding waste). The plan below is this library's
-// own: every cache block of the batch sits at a position on a cost line
-// (sequence b starts at P[b] and pays a fixed segment cost kappa before its
-// first block), and unit u takes the blocks whose position falls in
-// [u*W, (u+1)*W) with W = ceil(total / num_units). Every block therefore
-// belongs to exactly one unit, each unit's blocks are contiguous in
-// (sequence, block) order, and no unit costs more than W + kappa.
+// explainer section 2.4 on padding waste). The two plan shapes below are this
+// library's own (see mla_common.h): per-sequence runs for the streaming
+// kernel, a cost line cut into equal parts for the 128-row kernel. In both,
+// every cache block belongs to exactly one unit and a unit's blocks are
+// contiguous in (sequence, block) order.
 //
 // The device planner (one workgroup) and the host planner evaluate the same
-// integer formulas from mla_common.h, so their outputs agree bit for bit.
+// integer formulas, so their outputs agree bit for bit.
 #include "mla_common.h"
 
 namespace mla {
@@ -29,14 +27,13 @@ __device__ void block_inclusive_scan(int* a, int n, int* carry)
     for (int k = lo; k < hi; ++k) local += a[k];
     carry[tid] = local;
     __syncthreads();
-    // Hillis-Steele over the per-thread sums
     for (int off = 1; off < kPlanThreads; off <<= 1) {
         int v = (tid >= off) ? carry[tid - off] : 0;
         __syncthreads();
         carry[tid] += v;
         __syncthreads();
     }
-    int run = carry[tid] - local;        // exclusive offset of this thread's chunk
+    int run = carry[tid] - local;
     for (int k = lo; k < hi; ++k) {
         run += a[k];
         a[k] = run;
@@ -44,8 +41,14 @@ __device__ void block_inclusive_scan(int* a, int n, int* carry)
     __syncthreads();
 }
 
+__device__ __host__ inline void write_meta(int32_t* m, int b0, int j0, int b1, int j1, int split)
+{
+    m[0] = b0; m[1] = j0; m[2] = b1; m[3] = j1; m[4] = split;
+    m[5] = 0; m[6] = 0; m[7] = 0;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens, int batch,
-                                                             int kappa, int num_units,
+                                                             int rows_wg, int num_units,
                                                              int32_t* __restrict__ meta,
                                                              int32_t* __restrict__ splits)
 {
@@ -55,6 +58,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     int* carry = NS + (batch + 1);       // [kPlanThreads]
     const int tid = threadIdx.x;
 
+    if (plan_by_sequence(rows_wg)) {
+        // P = prefix sums of the block counts
+        for (int b = tid; b < batch; b += kPlanThreads) P[b + 1] = blocks_of(seqlens[b]);
+        if (tid == 0) P[0] = 0;
+        __syncthreads();
+        block_inclusive_scan(P + 1, batch, carry);
+        const int W = plan_width(P[batch], num_units - batch);
+        for (int b = tid; b < batch; b += kPlanThreads) NS[b + 1] = ceil_div(P[b + 1] - P[b], W);
+        if (tid == 0) NS[0] = 0;
+        __syncthreads();
+        block_inclusive_scan(NS + 1, batch, carry);
+        for (int b = tid; b <= batch; b += kPlanThreads) splits[b] = NS[b];
+        for (int u = tid; u < num_units; u += kPlanThreads) {
+            int32_t* m = meta + (size_t)u * kMetaInts;
+            int b = plan_owner(NS, batch, u);
+            if (b >= batch) { write_meta(m, batch, 0, batch, 0, 0); continue; }
+            int n = P[b + 1] - P[b];
+            int ns = NS[b + 1] - NS[b];
+            int k = u - NS[b];
+            write_meta(m, b, split_begin(n, ns, k), b, split_begin(n, ns, k + 1), k);
+        }
+        return;
+    }
+
+    const int kappa = kSegmentCost;
     for (int b = tid; b < batch; b += kPlanThreads) {
         int nb = blocks_of(seqlens[b]);
         P[b + 1] = nb > 0 ? nb + kappa : 0;
@@ -79,16 +107,32 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         plan_locate(P, batch, kappa, u * W, &b0, &j0);
         plan_locate(P, batch, kappa, (u + 1) * W, &b1, &j1);
         int split = (b0 < batch && (b0 != b1 || j0 != j1)) ? u - (P[b0] + kappa) / W : 0;
-        int32_t* m = meta + (size_t)u * kMetaInts;
-        m[0] = b0; m[1] = j0; m[2] = b1; m[3] = j1; m[4] = split;
-        m[5] = 0; m[6] = 0; m[7] = 0;
+        write_meta(meta + (size_t)u * kMetaInts, b0, j0, b1, j1, split);
     }
 }
 
-void plan_host(const int32_t* seqlens, int batch, int kappa, int num_units, int32_t* meta, int32_t* splits)
+void plan_host(const int32_t* seqlens, int batch, int rows_wg, int num_units, int32_t* meta, int32_t* splits)
 {
     int* P = new int[batch + 1];
     P[0] = 0;
+    if (plan_by_sequence(rows_wg)) {
+        for (int b = 0; b < batch; ++b) P[b + 1] = P[b] + blocks_of(seqlens[b]);
+        const int W = plan_width(P[batch], num_units - batch);
+        splits[0] = 0;
+        for (int b = 0; b < batch; ++b) splits[b + 1] = splits[b] + ceil_div(P[b + 1] - P[b], W);
+        for (int u = 0; u < num_units; ++u) {
+            int32_t* m = meta + (size_t)u * kMetaInts;
+            int b = plan_owner(splits, batch, u);
+            if (b >= batch) { write_meta(m, batch, 0, batch, 0, 0); continue; }
+            int n = P[b + 1] - P[b];
+            int ns = splits[b + 1] - splits[b];
+            int k = u - splits[b];
+            write_meta(m, b, split_begin(n, ns, k), b, split_begin(n, ns, k + 1), k);
+        }
+        delete[] P;
+        return;
+    }
+    const int kappa = kSegmentCost;
     for (int b = 0; b < batch; ++b) {
         int nb = blocks_of(seqlens[b]);
         P[b + 1] = P[b] + (nb > 0 ? nb + kappa : 0);
@@ -105,14 +149,12 @@ void plan_host(const int32_t* seqlens, int batch, int kappa, int num_units, int3
         plan_locate(P, batch, kappa, u * W, &b0, &j0);
         plan_locate(P, batch, kappa, (u + 1) * W, &b1, &j1);
         int split = (b0 < batch && (b0 != b1 || j0 != j1)) ? u - (P[b0] + kappa) / W : 0;
-        int32_t* m = meta + (size_t)u * kMetaInts;
-        m[0] = b0; m[1] = j0; m[2] = b1; m[3] = j1; m[4] = split;
-        m[5] = 0; m[6] = 0; m[7] = 0;
+        write_meta(meta + (size_t)u * kMetaInts, b0, j0, b1, j1, split);
     }
     delete[] P;
 }
 
-hipError_t launch_plan(const int32_t* seqlens, int batch, int kappa, int num_units, int32_t* meta,
+hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_units, int32_t* meta,
                        int32_t* splits, hipStream_t stream)
 {
     size_t lds = sizeof(int) * (2 * (size_t)(batch + 1) + kPlanThreads);
@@ -121,7 +163,7 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int kappa, int num_uni
                                            (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, stream, seqlens, batch, kappa,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, stream, seqlens, batch, rows_wg,
                        num_units, meta, splits);
     return hipGetLastError();
 }

@@ -122,10 +122,11 @@ def test_non_causal_multi_token():
     assert_parity(out, lse, ref_out, ref_lse, "non-causal")
 
 
-@pytest.mark.parametrize("units", [1, 2, 7, 2000])
-def test_plan_extremes_give_the_same_answer(units):
-    inp = cases.small_batch([1, 640, 65, 2000, 128], s_q=1, h_q=16, seed=17)
-    _say("plan with %d units" % units)
+@pytest.mark.parametrize("h_q,units", [(16, 6), (16, 7), (16, 40), (16, 2000), (128, 1), (128, 2), (128, 7),
+                                        (128, 300)])
+def test_plan_extremes_give_the_same_answer(h_q, units):
+    inp = cases.small_batch([1, 640, 65, 2000, 128], s_q=1, h_q=h_q, seed=17)
+    _say("plan with %d units, h_q=%d" % (units, h_q))
     out, lse, (meta, splits) = run_library(inp, num_units=units)
     ref_out, ref_lse = _oracle(inp)
     assert_parity(out, lse, ref_out, ref_lse, "units=%d" % units)
@@ -179,9 +180,10 @@ def test_device_plan_matches_host_plan(name):
     assert np.array_equal(dsplits.cpu().numpy(), hsplits)
 
 
-def test_device_plan_large_batch():
+@pytest.mark.parametrize("h_q,units", [(16, 5000 + 777), (128, 777)])
+def test_device_plan_large_batch(h_q, units):
     lens = np.random.default_rng(3).integers(0, 20000, 5000).astype(np.int32)
-    _say("plan B=5000")
-    dmeta, dsplits = mla.mla_get_metadata(torch.from_numpy(lens).cuda(), 16, 1, num_units=777)
-    hmeta, hsplits = mla.mla_get_metadata_host(lens, 16, 1, 777)
+    _say("plan B=5000 h_q=%d units=%d" % (h_q, units))
+    dmeta, dsplits = mla.mla_get_metadata(torch.from_numpy(lens).cuda(), h_q, 1, num_units=units)
+    hmeta, hsplits = mla.mla_get_metadata_host(lens, h_q, 1, units)
     assert np.array_equal(dmeta.cpu().numpy(), hmeta) and np.array_equal(dsplits.cpu().numpy(), hsplits)

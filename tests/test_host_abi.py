@@ -74,6 +74,7 @@ def _decode_args(**over):
     (dict(nblocks=0), MLA_ERR_INVALID_ARG),
     (dict(max_blocks=0), MLA_ERR_INVALID_ARG),
     (dict(units=0), MLA_ERR_INVALID_ARG),
+    (dict(units=2), MLA_ERR_INVALID_ARG),                        # per-sequence plan needs batch + 1
     (dict(scale=float("nan")), MLA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), MLA_ERR_INVALID_ARG),
     (dict(q=ctypes.c_void_p(0x10008)), MLA_ERR_INVALID_ARG),      # misaligned
@@ -96,11 +97,12 @@ def test_get_metadata_rejects_bad_arguments(lib):
 
 def test_plan_sizes(lib):
     s = mla.mla_plan_sizes(16, 1, 16, num_cus=256)
-    assert s["num_units"] == 256
-    assert s["meta_bytes"] == 256 * 8 * 4 and s["splits_bytes"] == 17 * 4
-    assert s["workspace_bytes"] == mla.mla_workspace_bytes(16, 1, 16, 256)
+    assert s["num_units"] == 256 + 16          # per-sequence plan: one extra unit per sequence
+    assert s["meta_bytes"] == 272 * 8 * 4 and s["splits_bytes"] == 17 * 4
+    assert s["workspace_bytes"] == mla.mla_workspace_bytes(16, 1, 16, 272)
     # h_q=128, s_q=2: 256 rows = two head groups of 128, so half the units
     assert mla.mla_plan_sizes(128, 2, 128, num_cus=256)["num_units"] == 128
+    assert mla.mla_plan_sizes(64, 1, 128, num_cus=256)["num_units"] == 256
     with pytest.raises(mla.MLAError):
         mla.mla_plan_sizes(4, 1, 10, num_cus=256)
 
@@ -111,21 +113,31 @@ def blocks(L):
     return (np.asarray(L, dtype=np.int64) + 63) // 64
 
 
+def kind_and_width(lens, s_q, h_q, units):
+    """Plan shape the library uses and its block budget per unit."""
+    rows = s_q * h_q
+    nb = blocks(lens)
+    if rows % 128 == 0:
+        kappa = 4
+        total = int(nb.sum()) + kappa * int((nb > 0).sum())
+        return "cost_line", kappa, max(1, -(-total // units))
+    return "by_sequence", 0, max(1, -(-int(nb.sum()) // (units - len(lens))))
+
+
 def check_plan(lens, s_q, h_q, units, meta, splits):
-    """Every block owned by exactly one unit, units contiguous, split counts consistent, balance bound."""
+    """Every block owned by exactly one unit, units contiguous, split counts and indices consistent,
+    balance bound of the plan shape."""
     lens = np.asarray(lens)
     B = len(lens)
     nb = blocks(lens)
+    kind, kappa, W = kind_and_width(lens, s_q, h_q, units)
     owner = {}
     touched = [set() for _ in range(B)]
-    rows = s_q * h_q
-    rows_wg = 128 if rows % 128 == 0 else 64 if rows % 64 == 0 else 32 if rows % 32 == 0 else 16
-    kappa = 1 + rows_wg // 32
-    total = int(nb.sum()) + kappa * int((nb > 0).sum())
-    W = max(1, -(-total // units))
     for u in range(units):
         b0, j0, b1, j1, split = (int(x) for x in meta[u, :5])
         assert (b0, j0) <= (b1, j1)
+        if kind == "by_sequence" and b0 < B:
+            assert b0 == b1, "a per-sequence unit spans sequences"
         cost = 0
         first = True
         b, j = b0, j0
@@ -148,7 +160,6 @@ def check_plan(lens, s_q, h_q, units, meta, splits):
     for b in range(B):
         for j in range(int(nb[b])):
             assert (b, j) in owner, (b, j)
-        # a sequence's blocks go to non-decreasing units
         us = [owner[(b, j)] for j in range(int(nb[b]))]
         assert us == sorted(us)
     ns = np.array([len(t) for t in touched])
@@ -164,6 +175,8 @@ def test_host_plan_properties(lib, seed):
     lens[rng.random(B) < 0.1] = 0
     s_q, h_q = [(1, 16), (2, 16), (1, 128), (2, 128), (3, 16), (1, 32), (2, 32)][seed % 7]
     units = int(rng.choice([1, 3, 64, 128, 256, 1000]))
+    if (s_q * h_q) % 128 != 0:
+        units += B
     meta, splits = mla.mla_get_metadata_host(lens, h_q, s_q, units)
     check_plan(lens, s_q, h_q, units, meta, splits)
 
@@ -180,6 +193,14 @@ def test_host_plan_workloads(lib):
 
 
 def test_host_plan_all_empty(lib):
-    meta, splits = mla.mla_get_metadata_host([0, 0, 0], 16, 1, 8)
-    assert np.array_equal(splits, [0, 0, 0, 0])
-    assert (meta[:, 0] == 3).all()          # every unit starts past the batch
+    for h_q in (16, 128):
+        meta, splits = mla.mla_get_metadata_host([0, 0, 0], h_q, 1, 8)
+        assert np.array_equal(splits, [0, 0, 0, 0])
+        assert (meta[:, 0] == 3).all()          # every unit starts past the batch
+
+
+def test_per_sequence_plan_needs_a_unit_per_sequence(lib):
+    with pytest.raises(mla.MLAError):
+        mla.mla_get_metadata_host([10, 20, 30], 16, 1, 3)
+    meta, splits = mla.mla_get_metadata_host([10, 20, 30], 16, 1, 4)
+    assert splits[-1] == 3
