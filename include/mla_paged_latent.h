@@ -103,10 +103,12 @@ int mla_workspace_bytes(int batch, int s_q, int h_q, int num_units, size_t* work
  * least batch + 1.
  *   cache_seqlens: device int32 [batch].
  *   tile_meta: device int32 [num_units, MLA_META_INTS], written. Row u is
- *     {b_begin, blk_begin, b_end, blk_end, split_index, 0, 0, 0}: unit u
- *     covers blocks (b, j) with (b_begin, blk_begin) <= (b, j) < (b_end,
- *     blk_end) in lexicographic order, j < ceil(L_b/64); split_index is how
- *     many earlier units touch sequence b_begin.
+ *     {b_begin, blk_begin, b_end, blk_end, split_index, L, slot, nsplit}:
+ *     unit u covers blocks (b, j) with (b_begin, blk_begin) <= (b, j) <
+ *     (b_end, blk_end) in lexicographic order, j < ceil(L_b/64); split_index
+ *     is how many earlier units touch sequence b_begin; L = cache_seqlens
+ *     [b_begin], slot = num_splits[b_begin] + split_index and nsplit = the
+ *     number of units touching b_begin (all three 0 for an empty unit).
  *   num_splits: device int32 [batch + 1], written: exclusive prefix sums of
  *     the number of units touching each sequence (0 for an empty sequence).
  * One small kernel on `stream`. The plan depends only on cache_seqlens,

@@ -93,10 +93,10 @@ int mla_plan_sizes(int batch, int s_q, int h_q, int num_cus, int* num_units, siz
     }
     const Geometry geo = geometry(s_q, h_q);
     // one workgroup per CU (the block buffers fill most of the LDS); a
-    // per-sequence plan adds one unit per sequence for the rounding of splits
+    // per-sequence plan needs at least one unit per sequence and one to spare
     int units = num_cus / geo.head_groups;
     if (units < 1) units = 1;
-    if (geo.by_sequence) units += batch;
+    if (geo.by_sequence && units < batch + 1) units = batch + 1;
     size_t part_o = 0, total = 0;
     workspace_layout(batch, geo.rows_total, units, &part_o, &total);
     if (num_units) *num_units = units;

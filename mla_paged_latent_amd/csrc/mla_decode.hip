@@ -56,6 +56,7 @@ typedef __attribute__((address_space(3))) s16x8 lds_s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_rw;
 
 constexpr int kLdsRow = 1168;            // LDS row stride: 72 data chunks + 1 pad chunk of 16 B
 constexpr int kRowSlots = 73;
@@ -98,6 +99,41 @@ __device__ __forceinline__ int sload(const int32_t* ptr)
     int v;
     asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
     return v;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Scalar load of 8 consecutive wave-uniform ints (one plan row).
+__device__ __forceinline__ i32x8 sload8(const int32_t* ptr)
+{
+    i32x8 v;
+    asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return v;
+}
+
+// Reductions across the lanes l, l^16, l^32, l^48 (one value per 16-lane row)
+// with the gfx950 lane-swap instructions: each swap exchanges whole 16- or
+// 32-lane halves between two operands, so combining both results pairs every
+// lane with its partner.
+__device__ __forceinline__ float xor32_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ unsigned lds_base(unsigned char* smem)
@@ -143,7 +179,6 @@ __device__ __forceinline__ void copy_rows(const unsigned char* gbase, int valid,
 constexpr int kSlotA = 19 * 1024;        // 16 rows x 1168 B, rounded up to whole 1 KB copies
 constexpr int kDmaA = 19;
 constexpr int kLdsA = 8 * kSlotA;        // two slots per wave: 155,648 B
-constexpr int kObufA = 16 * 516 * 4;     // one wave's 16 x 512 fp32 (row stride 516) merge region
 
 template <int NR>
 __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
@@ -156,13 +191,14 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     const int g = lane >> 4;
     const int c16 = lane & 15;
 
-    const int32_t* meta = p.meta + (size_t)blockIdx.x * kMetaInts;
-    const int b = sload(meta + 0);
-    const int j0 = sload(meta + 1);
-    const int j1 = sload(meta + 3);
-    const int split = sload(meta + 4);
+    const i32x8 meta = sload8(p.meta + (size_t)blockIdx.x * kMetaInts);
+    const int b = meta[0];
+    const int j0 = meta[1];
+    const int j1 = meta[3];
+    const int L = meta[5];
+    const int slot = meta[6];
+    const int nsplit = meta[7];
     if (b >= p.batch || j0 >= j1) return;
-    const int L = sload(p.seqlens + b);
     const int tok_begin = j0 * kPage;
     const int tok_end = min(j1 * kPage, L);
     const int nsub = (tok_end - tok_begin + 15) >> 4;
@@ -170,19 +206,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
     const int npages = j1 - j0;
     const int page_vec = lane < npages ? table[j0 + lane] : 0;
-
-    bf16x8 qf[NR][18];
-    int lim[NR];
-#pragma unroll
-    for (int rt = 0; rt < NR; ++rt) {
-        const int row = blockIdx.y * R + rt * 16 + c16;
-        const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + row) * kDqk + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, *(const s16x8*)(qrow + 32 * ks));
-        const int iq = row / p.h_q;
-        lim[rt] = min(tok_end, p.causal ? L - (p.s_q - 1 - iq) : L);
-    }
-    settle_loads();
 
     float mrun[NR], lrun[NR];
     f32x4 acc[NR][32];
@@ -207,6 +230,21 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     if (K > 0) issue(0);
     if (K > 1) issue(1);
 
+    // queries (issued after the first copies; the settle below waits for both)
+    bf16x8 qf[NR][18];
+    int lim[NR];
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+        const int row = blockIdx.y * R + rt * 16 + c16;
+        const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + row) * kDqk + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, *(const s16x8*)(qrow + 32 * ks));
+        const int iq = row / p.h_q;
+        lim[rt] = min(tok_end, p.causal ? L - (p.s_q - 1 - iq) : L);
+    }
+    settle_loads();
+
+
     const unsigned a_off = (unsigned)(token_of_row(c16) * kLdsRow + g * 16);
     const unsigned v_off = (unsigned)(token_of_row(4 * g + (c16 >> 2)) * kLdsRow + 8 * (c16 & 3));
     for (int k = 0; k < K; ++k) {
@@ -214,16 +252,31 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
         const unsigned sb = slot0 + (unsigned)(k & 1) * kSlotA;
         const int tok0 = tok_begin + 16 * (wave + 4 * k);
 
-        // S^T = K Q^T for 16 tokens x R rows
+        // every LDS read of this slot up front: 18 K chunks (QK^T A operand) and
+        // 32 transposed V pieces (PV A operand)
+        s16x8 ka[18];
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) ka[ks] = lds_load16(sb + a_off + 64 * ks);
+        s16x4 va[32];
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) va[nt] = lds_tr4(sb + v_off + 32 * nt);
+
+        // S^T = K Q^T for 16 tokens x R rows, two accumulation chains
         f32x4 s[NR];
 #pragma unroll
-        for (int rt = 0; rt < NR; ++rt) s[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < NR; ++rt) {
+            f32x4 e0 = {0.f, 0.f, 0.f, 0.f}, e1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, lds_load16(sb + a_off + 64 * ks));
-#pragma unroll
-            for (int rt = 0; rt < NR; ++rt) s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][ks], s[rt], 0, 0, 0);
+            for (int ks = 0; ks < 18; ks += 2) {
+                e0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[ks]), qf[rt][ks], e0, 0, 0, 0);
+                e1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[ks + 1]), qf[rt][ks + 1], e1, 0, 0, 0);
+            }
+            s[rt] = e0 + e1;
         }
+
+        // the slot's reads are done: refill it with sub-tile k + 2
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (k + 2 < K) issue(k + 2);
 
         // scale, mask, online softmax; s[rt][i] is token tok0 + token_of_row(4g + i)
         s16x4 pb[NR];
@@ -237,8 +290,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
                 s[rt][i] = v;
                 tmax = fmaxf(tmax, v);
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = xor32_max(xor16_max(tmax));
             const bool need = tmax > mrun[rt] + kLazyTau;
             if (wave_any(need)) {
                 const float mnew = need ? tmax : mrun[rt];
@@ -256,93 +308,89 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
                 psum += pv;
                 pb[rt][i] = (short)bf16_rne(pv);
             }
-            psum += __shfl_xor(psum, 16);
-            psum += __shfl_xor(psum, 32);
-            lrun[rt] += psum;
+            lrun[rt] += xor32_sum(xor16_sum(psum));
         }
 
         // O^T += V^T P^T
 #pragma unroll
         for (int nt = 0; nt < 32; ++nt) {
-            const s16x4 va = lds_tr4(sb + v_off + 32 * nt);
 #pragma unroll
-            for (int rt = 0; rt < NR; ++rt) acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][nt], 0, 0, 0);
+            for (int rt = 0; rt < NR; ++rt) acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[nt], pb[rt], acc[rt][nt], 0, 0, 0);
         }
-
-        if (k + 2 < K) issue(k + 2);
     }
 
-    // ---- merge the four waves' (m, l, O) and write the result
-    wg_barrier();
-    lds_f32* stat_m = (lds_f32*)(uintptr_t)lds0;          // [4][R]
-    lds_f32* stat_l = stat_m + 4 * R;                       // [4][R]
-    const unsigned obuf0 = lds0 + 1024;                    // 4 regions of kObufA
+    // ---- merge the four waves' (m, l, O) and write the result. Wave w owns
+    // output tiles nt in [8w, 8w + 8) (dims [128w, 128w + 128)) and keeps them
+    // in registers; it posts its other 24 tiles to LDS as bf16 (unscaled) for
+    // their owners, and its running max/sum for every row.
+    wg_barrier();                                            // every wave is done with its slots
+    lds_f32* stat_m = (lds_f32*)(uintptr_t)lds0;            // [4][R]
+    lds_f32* stat_l = stat_m + 4 * R;                         // [4][R]
+    const unsigned xbuf = lds0 + 1024;                       // [4][NR][32 tiles][64 lanes] x 8 B
     if (g == 0) {
 #pragma unroll
-        for (int rt = 0; rt < NR; ++rt) stat_m[wave * R + rt * 16 + c16] = mrun[rt];
+        for (int rt = 0; rt < NR; ++rt) {
+            stat_m[wave * R + rt * 16 + c16] = mrun[rt];
+            stat_l[wave * R + rt * 16 + c16] = lrun[rt];
+        }
     }
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) {
+            if ((nt >> 3) == wave) continue;
+            s16x4 v;
+            v[0] = (short)bf16_rne(acc[rt][nt][0]);
+            v[1] = (short)bf16_rne(acc[rt][nt][1]);
+            v[2] = (short)bf16_rne(acc[rt][nt][2]);
+            v[3] = (short)bf16_rne(acc[rt][nt][3]);
+            *(lds_s16x4_rw*)(uintptr_t)(xbuf + (unsigned)((((wave * NR + rt) * 32 + nt) * 64 + lane) * 8)) = v;
+        }
     wg_barrier();
-    float fac[NR];
 #pragma unroll
     for (int rt = 0; rt < NR; ++rt) {
-        float mall = -INFINITY;
+        const int rrow = rt * 16 + c16;
+        float mw[4], mall = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) mall = fmaxf(mall, stat_m[w * R + rt * 16 + c16]);
-        fac[rt] = mrun[rt] == -INFINITY ? 0.f : exp2f(mrun[rt] - mall);
-    }
-    if (g == 0) {
+        for (int w = 0; w < 4; ++w) {
+            mw[w] = stat_m[w * R + rrow];
+            mall = fmaxf(mall, mw[w]);
+        }
+        float fw[4], lt = 0.f;
 #pragma unroll
-        for (int rt = 0; rt < NR; ++rt) stat_l[wave * R + rt * 16 + c16] = lrun[rt] * fac[rt];
-    }
-    const int nsplit = sload(p.splits + b + 1) - sload(p.splits + b);
-    const int slot = sload(p.splits + b) + split;
+        for (int w = 0; w < 4; ++w) {
+            fw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - mall);
+            lt += stat_l[w * R + rrow] * fw[w];
+        }
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int grow = blockIdx.y * R + rrow;
 #pragma unroll
-    for (int rt = 0; rt < NR; ++rt) {
-        const unsigned mine = obuf0 + (unsigned)wave * kObufA + (unsigned)(c16 * 2064 + 16 * g);
-#pragma unroll
-        for (int nt = 0; nt < 32; ++nt) *(lds_f32x4*)(uintptr_t)(mine + 64 * nt) = acc[rt][nt] * fac[rt];
-        wg_barrier();
-        // wave w finishes dims [128 w, 128 w + 128) of the 16 rows of tile rt
-        for (int idx = lane; idx < 256; idx += 64) {
-            const int r = idx >> 4;
-            const int d = 128 * wave + 8 * (idx & 15);
-            f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-            float lt = 0.f;
+        for (int nt = 0; nt < 32; ++nt) {
+            if ((nt >> 3) != wave) continue;                  // static tile index, uniform branch
+            f32x4 v = acc[rt][nt] * fw[nt >> 3];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const unsigned src = obuf0 + (unsigned)w * kObufA + (unsigned)(r * 2064 + d * 4);
-                v0 += *(const lds_f32x4*)(uintptr_t)src;
-                v1 += *(const lds_f32x4*)(uintptr_t)(src + 16);
-                lt += stat_l[w * R + rt * 16 + r];
+                if (w == wave) continue;
+                const s16x4 o = *(const lds_s16x4_rw*)(uintptr_t)(
+                    xbuf + (unsigned)((((w * NR + rt) * 32 + nt) * 64 + lane) * 8));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] += __uint_as_float((unsigned)(unsigned short)o[i] << 16) * fw[w];
             }
-            const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            const int grow = blockIdx.y * R + rt * 16 + r;
+            v *= inv;
+            const int d = 16 * nt + 4 * g;
             if (nsplit == 1) {
-                s16x8 o;
-                o[0] = bf16_rne(v0[0] * inv); o[1] = bf16_rne(v0[1] * inv);
-                o[2] = bf16_rne(v0[2] * inv); o[3] = bf16_rne(v0[3] * inv);
-                o[4] = bf16_rne(v1[0] * inv); o[5] = bf16_rne(v1[1] * inv);
-                o[6] = bf16_rne(v1[2] * inv); o[7] = bf16_rne(v1[3] * inv);
-                *(s16x8*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = o;
+                ushort4 ob;
+                ob.x = bf16_rne(v[0]); ob.y = bf16_rne(v[1]); ob.z = bf16_rne(v[2]); ob.w = bf16_rne(v[3]);
+                *(ushort4*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = ob;
             } else {
-                float* o = p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d;
-                *(f32x4*)o = v0 * inv;
-                *(f32x4*)(o + 4) = v1 * inv;
+                *(f32x4*)(p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d) = v;
             }
         }
-        if (wave == 0 && lane < 16) {
-            float lt = 0.f, mx = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                lt += stat_l[w * R + rt * 16 + lane];
-                mx = fmaxf(mx, stat_m[w * R + rt * 16 + lane]);
-            }
-            const float lse = lt > 0.f ? (mx + __log2f(lt)) * kLn2 : -INFINITY;
-            const int grow = blockIdx.y * R + rt * 16 + lane;
+        if (wave == 0 && g == 0) {
+            const float lse = lt > 0.f ? (mall + __log2f(lt)) * kLn2 : -INFINITY;
             if (nsplit == 1) p.lse[(size_t)b * p.rows_total + grow] = lse;
             else p.part_lse[(size_t)slot * p.rows_total + grow] = lse;
         }
-        if (rt + 1 < NR) wg_barrier();
     }
 }
 
@@ -398,6 +446,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     const int b1 = sload(meta + 2);
     const int j1 = sload(meta + 3);
     const int split0 = sload(meta + 4);
+    const int first_slot = sload(meta + 6);
 
     const int row = blockIdx.y * 128 + 32 * wave + r32;     // this lane's query row
     const int iq = row / p.h_q;
@@ -536,7 +585,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
         if (ctok >= cs.te) {
             // end of segment: write this wave's 32 rows
             const int nsplit = sload(p.splits + cs.b + 1) - sload(p.splits + cs.b);
-            const int slot = sload(p.splits + cs.b) + (cs.b == b0 ? split0 : 0);
+            const int slot = cs.b == b0 ? first_slot : sload(p.splits + cs.b);
             const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
             if (nsplit == 1) {
                 uint16_t* o = p.out + ((size_t)cs.b * p.rows_total + row) * kDv + 4 * h;
@@ -582,6 +631,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
 // the decode kernel.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
 {
+    constexpr int U = 8;                                    // partials in flight per thread
     const int t = threadIdx.x & 127;                        // 4-dim chunk of the row
     const int row = blockIdx.x * 2 + (threadIdx.x >> 7);
     const int b = blockIdx.y;
@@ -591,8 +641,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
     if (ns == 1) return;
     uint16_t* o = p.out + ((size_t)b * p.rows_total + row) * kDv + 4 * t;
     float* lo = p.lse + (size_t)b * p.rows_total + row;
+    const float* lse_col = p.part_lse + (size_t)s0 * p.rows_total + row;
     float mx = -INFINITY;
-    for (int k = 0; k < ns; ++k) mx = fmaxf(mx, p.part_lse[(size_t)(s0 + k) * p.rows_total + row]);
+    for (int k = 0; k < ns; k += U) {
+        float w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = (k + u < ns) ? lse_col[(size_t)(k + u) * p.rows_total] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, w[u]);
+    }
     if (ns == 0 || mx == -INFINITY) {
         *(ushort4*)o = make_ushort4(0, 0, 0, 0);
         if (t == 0) *lo = -INFINITY;
@@ -600,28 +657,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
     }
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    int k = 0;
-    for (; k + 4 <= ns; k += 4) {
-        f32x4 v[4];
-        float w[4];
+    const float* o_col = p.part_o + ((size_t)s0 * p.rows_total + row) * kDv + 4 * t;
+    for (int k = 0; k < ns; k += U) {
+        f32x4 v[U];
+        float w[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const size_t sr = (size_t)(s0 + k + u) * p.rows_total + row;
-            w[u] = p.part_lse[sr];
-            v[u] = *(const f32x4*)(p.part_o + sr * kDv + 4 * t);
+        for (int u = 0; u < U; ++u) {
+            const bool ok = k + u < ns;
+            w[u] = ok ? lse_col[(size_t)(k + u) * p.rows_total] : -INFINITY;
+            v[u] = ok ? *(const f32x4*)(o_col + (size_t)(k + u) * p.rows_total * kDv) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
             const float e = __expf(w[u] - mx);
             wsum += e;
             a += v[u] * e;
         }
-    }
-    for (; k < ns; ++k) {
-        const size_t sr = (size_t)(s0 + k) * p.rows_total + row;
-        const float e = __expf(p.part_lse[sr] - mx);
-        wsum += e;
-        a += *(const f32x4*)(p.part_o + sr * kDv + 4 * t) * e;
     }
     const float inv = 1.f / wsum;
     ushort4 r;

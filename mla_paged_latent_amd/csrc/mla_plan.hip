@@ -41,10 +41,16 @@ __device__ void block_inclusive_scan(int* a, int n, int* carry)
     __syncthreads();
 }
 
-__device__ __host__ inline void write_meta(int32_t* m, int b0, int j0, int b1, int j1, int split)
+// Row u of the plan: {b_begin, blk_begin, b_end, blk_end, split index of the
+// first segment, cache_seqlens[b_begin], partial slot of the first segment
+// (num_splits[b_begin] + split index), number of splits of b_begin}. The last
+// three are zero for an empty unit; they spare the decode kernel dependent
+// loads at its start and end.
+__device__ __host__ inline void write_meta(int32_t* m, int b0, int j0, int b1, int j1, int split, int len,
+                                           int first_slot, int nsplit)
 {
     m[0] = b0; m[1] = j0; m[2] = b1; m[3] = j1; m[4] = split;
-    m[5] = 0; m[6] = 0; m[7] = 0;
+    m[5] = len; m[6] = first_slot; m[7] = nsplit;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens, int batch,
@@ -73,11 +79,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         for (int u = tid; u < num_units; u += kPlanThreads) {
             int32_t* m = meta + (size_t)u * kMetaInts;
             int b = plan_owner(NS, batch, u);
-            if (b >= batch) { write_meta(m, batch, 0, batch, 0, 0); continue; }
+            if (b >= batch) { write_meta(m, batch, 0, batch, 0, 0, 0, 0, 0); continue; }
             int n = P[b + 1] - P[b];
             int ns = NS[b + 1] - NS[b];
             int k = u - NS[b];
-            write_meta(m, b, split_begin(n, ns, k), b, split_begin(n, ns, k + 1), k);
+            write_meta(m, b, split_begin(n, ns, k), b, split_begin(n, ns, k + 1), k, seqlens[b], NS[b] + k, ns);
         }
         return;
     }
@@ -106,8 +112,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         int b0, j0, b1, j1;
         plan_locate(P, batch, kappa, u * W, &b0, &j0);
         plan_locate(P, batch, kappa, (u + 1) * W, &b1, &j1);
-        int split = (b0 < batch && (b0 != b1 || j0 != j1)) ? u - (P[b0] + kappa) / W : 0;
-        write_meta(meta + (size_t)u * kMetaInts, b0, j0, b1, j1, split);
+        const bool any = b0 < batch && (b0 != b1 || j0 != j1);
+        int split = any ? u - (P[b0] + kappa) / W : 0;
+        write_meta(meta + (size_t)u * kMetaInts, b0, j0, b1, j1, split, any ? seqlens[b0] : 0,
+                   any ? NS[b0] + split : 0, any ? NS[b0 + 1] - NS[b0] : 0);
     }
 }
 
@@ -123,11 +131,11 @@ void plan_host(const int32_t* seqlens, int batch, int rows_wg, int num_units, in
         for (int u = 0; u < num_units; ++u) {
             int32_t* m = meta + (size_t)u * kMetaInts;
             int b = plan_owner(splits, batch, u);
-            if (b >= batch) { write_meta(m, batch, 0, batch, 0, 0); continue; }
+            if (b >= batch) { write_meta(m, batch, 0, batch, 0, 0, 0, 0, 0); continue; }
             int n = P[b + 1] - P[b];
             int ns = splits[b + 1] - splits[b];
             int k = u - splits[b];
-            write_meta(m, b, split_begin(n, ns, k), b, split_begin(n, ns, k + 1), k);
+            write_meta(m, b, split_begin(n, ns, k), b, split_begin(n, ns, k + 1), k, seqlens[b], splits[b] + k, ns);
         }
         delete[] P;
         return;
@@ -148,8 +156,10 @@ void plan_host(const int32_t* seqlens, int batch, int rows_wg, int num_units, in
         int b0, j0, b1, j1;
         plan_locate(P, batch, kappa, u * W, &b0, &j0);
         plan_locate(P, batch, kappa, (u + 1) * W, &b1, &j1);
-        int split = (b0 < batch && (b0 != b1 || j0 != j1)) ? u - (P[b0] + kappa) / W : 0;
-        write_meta(meta + (size_t)u * kMetaInts, b0, j0, b1, j1, split);
+        const bool any = b0 < batch && (b0 != b1 || j0 != j1);
+        int split = any ? u - (P[b0] + kappa) / W : 0;
+        write_meta(meta + (size_t)u * kMetaInts, b0, j0, b1, j1, split, any ? seqlens[b0] : 0,
+                   any ? splits[b0] + split : 0, any ? splits[b0 + 1] - splits[b0] : 0);
     }
     delete[] P;
 }

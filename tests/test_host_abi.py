@@ -97,9 +97,10 @@ def test_get_metadata_rejects_bad_arguments(lib):
 
 def test_plan_sizes(lib):
     s = mla.mla_plan_sizes(16, 1, 16, num_cus=256)
-    assert s["num_units"] == 256 + 16          # per-sequence plan: one extra unit per sequence
-    assert s["meta_bytes"] == 272 * 8 * 4 and s["splits_bytes"] == 17 * 4
-    assert s["workspace_bytes"] == mla.mla_workspace_bytes(16, 1, 16, 272)
+    assert s["num_units"] == 256
+    assert s["meta_bytes"] == 256 * 8 * 4 and s["splits_bytes"] == 17 * 4
+    assert s["workspace_bytes"] == mla.mla_workspace_bytes(16, 1, 16, 256)
+    assert mla.mla_plan_sizes(300, 1, 16, num_cus=256)["num_units"] == 301
     # h_q=128, s_q=2: 256 rows = two head groups of 128, so half the units
     assert mla.mla_plan_sizes(128, 2, 128, num_cus=256)["num_units"] == 128
     assert mla.mla_plan_sizes(64, 1, 128, num_cus=256)["num_units"] == 256
@@ -165,6 +166,13 @@ def check_plan(lens, s_q, h_q, units, meta, splits):
     ns = np.array([len(t) for t in touched])
     assert splits[0] == 0 and np.array_equal(np.diff(splits), ns)
     assert splits[-1] <= units + B
+    # trailing fields: length, partial slot and split count of the first sequence
+    for u in range(units):
+        b0, j0, b1, j1, split, L, slot, nsplit = (int(x) for x in meta[u])
+        if b0 < B and (b0, j0) != (b1, j1):
+            assert L == lens[b0] and slot == splits[b0] + split and nsplit == ns[b0]
+        else:
+            assert (L, slot, nsplit) == (0, 0, 0)
 
 
 @pytest.mark.parametrize("seed", range(12))
