@@ -96,7 +96,7 @@ int mla_workspace_bytes(int batch, int s_q, int h_q, int num_units, size_t* work
  * kernel is tuned for variable-length serving: GeekNews release note).
  * Each unit is one workgroup's run of cache blocks, contiguous in (sequence,
  * block) order; every block belongs to exactly one unit. When s_q*h_q is a
- * multiple of 128 the blocks, with a fixed extra cost per sequence, are cut
+ * multiple of 64 the blocks, with a fixed extra cost per sequence, are cut
  * into num_units runs of near-equal cost (a run may span sequences);
  * otherwise each sequence is cut into near-equal runs of at most
  * ceil(total_blocks / (num_units - batch)) blocks, and num_units must be at

@@ -16,28 +16,28 @@ constexpr int kPageBytes = kPage * kRowBytes;   // 73,728 B, contiguous in HBM
 constexpr int kMetaInts = 8;
 constexpr int kMaxRows = 1024;     // largest s_q*h_q accepted
 
-// Query rows per workgroup: 128 when s_q*h_q is a multiple of 128 (the
-// 32x32-MFMA kernel, four waves of 32 rows), else 16 (the streaming kernel,
-// every wave holds all 16 rows). Rows beyond that are covered by more
-// workgroups ("head groups") reading the same cache blocks.
+// Query rows per workgroup: 64 when s_q*h_q is a multiple of 64 (the
+// 32x32-MFMA kernel: two row groups of 32, each split over two waves), else
+// 16 (the streaming kernel, every wave holds all 16 rows). Rows beyond that
+// are covered by more workgroups ("head groups") reading the same blocks.
 inline __host__ __device__ int rows_per_wg(int rows_total)
 {
-    return rows_total % 128 == 0 ? 128 : 16;
+    return rows_total % 64 == 0 ? 64 : 16;
 }
 
 // Two plan shapes.
 //  * Streaming kernel (16 rows): every unit is one sequence's run of blocks.
 //    W = ceil(total_blocks / G) blocks at most per unit; sequence b is cut into
 //    ns_b = ceil(n_b / W) near-equal runs. Units number sum(ns_b) <= G + B.
-//  * 128-row kernel: blocks of the batch, in (sequence, block) order, sit on a
+//  * 64-row kernel: blocks of the batch, in (sequence, block) order, sit on a
 //    cost line where sequence b starts at P[b] and pays a fixed segment cost
 //    kappa before its first block; unit u owns the blocks whose position lies
 //    in [u*W, (u+1)*W), W = ceil(C / G). A unit may span several sequences.
-inline __host__ __device__ bool plan_by_sequence(int rows_wg) { return rows_wg < 128; }
+inline __host__ __device__ bool plan_by_sequence(int rows_wg) { return rows_wg < 64; }
 
-// Fixed cost of one (unit, sequence) segment of the 128-row kernel, in cache
-// blocks: reloading 128 query rows and writing 128 result rows costs about
-// this much traffic.
+// Fixed cost of one (unit, sequence) segment of the 64-row kernel, in cache
+// blocks: reloading 64 query rows and writing 64 result rows costs about this
+// much traffic.
 constexpr int kSegmentCost = 4;
 
 inline __host__ __device__ int blocks_of(int len) { return len > 0 ? (len + kPage - 1) / kPage : 0; }

@@ -4,7 +4,7 @@
 // of varying length (GeekNews release note, id.news.hada.io; FlashMLA
 // explainer section 2.4 on padding waste). The two plan shapes below are this
 // library's own (see mla_common.h): per-sequence runs for the streaming
-// kernel, a cost line cut into equal parts for the 128-row kernel. In both,
+// kernel, a cost line cut into equal parts for the 64-row kernel. In both,
 // every cache block belongs to exactly one unit and a unit's blocks are
 // contiguous in (sequence, block) order.
 //

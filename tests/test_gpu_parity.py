@@ -93,11 +93,12 @@ SHAPES = [
     ([1, 63, 64, 65, 127, 128, 129, 300], 1, 16),
     ([1, 2, 64, 65, 200], 2, 16),            # 32 rows, causal over 2 new tokens
     ([100, 257, 64], 1, 32),
-    ([33, 130, 1000], 1, 64),
-    ([70, 190], 2, 32),                      # 64 rows
-    ([5, 129, 700], 1, 128),
-    ([3, 66, 500], 4, 32),                   # 128 rows
-    ([2, 65, 300], 2, 128),                  # 256 rows: two head groups
+    ([33, 130, 1000], 1, 64),                # 64 rows: the wide kernel
+    ([70, 190], 2, 32),                      # 64 rows, causal
+    ([5, 129, 700], 1, 128),                 # two head groups of 64
+    ([3, 66, 500], 4, 32),                   # 128 rows, causal over 4 new tokens
+    ([2, 65, 300], 2, 128),                  # 256 rows: four head groups
+    ([7, 64, 0, 900], 3, 64),                # 192 rows, an empty sequence
     ([10, 140], 3, 16),                      # 48 rows: three head groups of 16
     ([1, 2, 3], 4, 16),                      # queries that see no token (L < s_q)
     ([0, 50, 0, 64], 1, 16),                 # empty sequences

@@ -101,9 +101,12 @@ def test_plan_sizes(lib):
     assert s["meta_bytes"] == 256 * 8 * 4 and s["splits_bytes"] == 17 * 4
     assert s["workspace_bytes"] == mla.mla_workspace_bytes(16, 1, 16, 256)
     assert mla.mla_plan_sizes(300, 1, 16, num_cus=256)["num_units"] == 301
-    # h_q=128, s_q=2: 256 rows = two head groups of 128, so half the units
-    assert mla.mla_plan_sizes(128, 2, 128, num_cus=256)["num_units"] == 128
-    assert mla.mla_plan_sizes(64, 1, 128, num_cus=256)["num_units"] == 256
+    # 64 query rows per workgroup: h_q=128, s_q=2 is 256 rows = four head groups
+    assert mla.mla_plan_sizes(128, 2, 128, num_cus=256)["num_units"] == 64
+    assert mla.mla_plan_sizes(64, 1, 128, num_cus=256)["num_units"] == 128
+    assert mla.mla_plan_sizes(64, 1, 64, num_cus=256)["num_units"] == 256
+    # 48 rows: three head groups of 16, per-sequence plan
+    assert mla.mla_plan_sizes(8, 3, 16, num_cus=256)["num_units"] == 85
     with pytest.raises(mla.MLAError):
         mla.mla_plan_sizes(4, 1, 10, num_cus=256)
 
@@ -118,7 +121,7 @@ def kind_and_width(lens, s_q, h_q, units):
     """Plan shape the library uses and its block budget per unit."""
     rows = s_q * h_q
     nb = blocks(lens)
-    if rows % 128 == 0:
+    if rows % 64 == 0:
         kappa = 4
         total = int(nb.sum()) + kappa * int((nb > 0).sum())
         return "cost_line", kappa, max(1, -(-total // units))
@@ -181,9 +184,9 @@ def test_host_plan_properties(lib, seed):
     B = int(rng.integers(1, 300))
     lens = rng.integers(0, 5000, B)
     lens[rng.random(B) < 0.1] = 0
-    s_q, h_q = [(1, 16), (2, 16), (1, 128), (2, 128), (3, 16), (1, 32), (2, 32)][seed % 7]
+    s_q, h_q = [(1, 16), (2, 16), (1, 128), (2, 128), (3, 16), (1, 32), (2, 32), (1, 64)][seed % 8]
     units = int(rng.choice([1, 3, 64, 128, 256, 1000]))
-    if (s_q * h_q) % 128 != 0:
+    if (s_q * h_q) % 64 != 0:
         units += B
     meta, splits = mla.mla_get_metadata_host(lens, h_q, s_q, units)
     check_plan(lens, s_q, h_q, units, meta, splits)
