@@ -40,13 +40,17 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
 MALL_BYTES = 256 * 2 ** 20
-DECODE_SRC = os.path.join(ROOT, "mla_paged_latent_amd", "csrc", "mla_decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "mla_paged_latent_amd", "csrc", f)
+               for f in ("mla_decode.hip", "mla_decode_wide.hip", "mla_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
 def kernel_source_digest() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

@@ -26,6 +26,12 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-source extra flags. The wide decode kernel uses the VGPR form of the
+# matrix ops, so its output accumulators can be rescaled in place.
+FILE_FLAGS = {
+    "mla_decode_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -46,7 +52,7 @@ def build(verbose: bool = False, out: Path = LIB, extra_flags=()) -> Path:
     cc = hipcc()
     for src in sources():
         obj = objdir / (src.stem + ".o")
-        cmd = [cc, *HIPCC_FLAGS, *extra_flags, "-I", str(ROOT / "include"), "-c", str(src), "-o", str(obj)]
+        cmd = [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(src.name, []), *extra_flags, "-I", str(ROOT / "include"), "-c", str(src), "-o", str(obj)]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,140 @@
+// Device-side building blocks shared by the decode kernels (gfx950): vector
+// types, direct global->LDS copies, explicit wait counts, scalar loads of
+// wave-uniform values, cross-lane reductions and LDS access helpers.
+#pragma once
+
+#include "mla_common.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) s16x8 lds_s16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_rw;
+
+constexpr int kChunks = 72;
+constexpr float kLazyTau = 8.f;          // exp2-domain slack of the running max
+constexpr float kLn2 = 0.69314718055994531f;
+
+// ---------------------------------------------------------------- primitives
+
+// One 16-byte global->LDS copy per lane. lds_addr (uniform) is the LDS byte
+// address of the wave's 1 KB destination; lane l lands at lds_addr + 16 l.
+// Issued through asm so the compiler does not order later LDS reads of other
+// buffers behind it; completion is awaited explicitly with vmcnt.
+__device__ __forceinline__ void dma16(const unsigned char* gptr, unsigned lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory");
+}
+
+// One 16-byte global->LDS copy per lane from a wave-uniform base plus a
+// per-lane 32-bit byte offset (the scalar-base form of the copy).
+__device__ __forceinline__ void dma16s(const unsigned char* sbase, unsigned voff, unsigned lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory");
+}
+
+#define MLA_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+
+// vmcnt(0) issued through the builtin, which the compiler's own wait-count
+// tracking sees: after it, loads the compiler issued (queries, table rows) are
+// known complete, so it inserts no waits for them inside the copy pipeline
+// (such a wait would also stall on every block copy in flight).
+__device__ __forceinline__ void settle_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ void wg_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Scalar load of a wave-uniform int (waits for it in the same asm block).
+__device__ __forceinline__ int sload(const int32_t* ptr)
+{
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return v;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Scalar load of 8 consecutive wave-uniform ints (one plan row).
+__device__ __forceinline__ i32x8 sload8(const int32_t* ptr)
+{
+    i32x8 v;
+    asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return v;
+}
+
+// Reductions across the lanes l, l^16, l^32, l^48 (one value per 16-lane row)
+// with the gfx950 lane-swap instructions: each swap exchanges whole 16- or
+// 32-lane halves between two operands, so combining both results pairs every
+// lane with its partner.
+__device__ __forceinline__ float xor32_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ unsigned lds_base(unsigned char* smem)
+{
+    return (unsigned)(uintptr_t)(lds_u8*)smem;
+}
+
+__device__ __forceinline__ s16x8 lds_load16(unsigned addr) { return *(const lds_s16x8*)(uintptr_t)addr; }
+
+__device__ __forceinline__ s16x4 lds_tr4(unsigned addr)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
+}
+
+__device__ __forceinline__ int token_of_row(int a) { return ((a >> 3) << 3) + ((a & 3) << 1) + ((a >> 2) & 1); }
+
+__device__ __forceinline__ unsigned short bf16_rne(float f)
+{
+    unsigned u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (unsigned short)(u >> 16);
+}
+
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b)
+{
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+}  // namespace mla
