@@ -87,6 +87,58 @@ def cpu_baseline(inp, nbytes_total, min_seconds=10.0, max_reps=50):
                       % (reps, inp.name, inp.batch, el)}
 
 
+def _counter_means(csv_dir, counter, name_part):
+    """Mean value of `counter` per dispatch of kernels whose name contains name_part,
+    from a rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+    vals = []
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter and name_part in row["Kernel_Name"]:
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no %s samples for kernels matching %r under %s" % (counter, name_part, csv_dir))
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(args):
+    """Turn FETCH_SIZE / WRITE_SIZE counter runs of the decode kernel, and the same counters
+    over a plain device copy of known size, into HBM bytes per decode launch; stored in
+    profiles/decode_traffic.json under the workload's name."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.pmc_summary
+    kname = "decode_wide_kernel" if args.workload in ("compute_bound", "mixed") else "decode_stream_kernel"
+    copy_bytes = args.copy_bytes
+    cf, _ = _counter_means(cfetch_dir, "FETCH_SIZE", "copy")
+    cw, _ = _counter_means(cwrite_dir, "WRITE_SIZE", "copy")
+    f_fetch = copy_bytes / (cf * 1024.0)       # counters are in KiB
+    f_write = copy_bytes / (cw * 1024.0)
+    kf, nf = _counter_means(fetch_dir, "FETCH_SIZE", kname)
+    kw, nw = _counter_means(write_dir, "WRITE_SIZE", kname)
+    ent = {
+        "kernel": kname,
+        "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kw, 1),
+        "dispatches": [nf, nw],
+        "copy_calibration_bytes": copy_bytes,
+        "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+        "factor_fetch": round(f_fetch, 4), "factor_write": round(f_write, 4),
+        "hbm_bytes_per_launch": int(kf * 1024.0 * f_fetch + kw * 1024.0 * f_write),
+        "kernel_source_sha": kernel_source_digest(),
+    }
+    try:
+        with open(TRAFFIC_FILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        doc = {}
+    doc[args.workload] = ent
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(doc, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({args.workload: ent}))
+    return 0
+
+
 def inp_flops(inp):
     return wl.algorithmic_counts(inp.cache_seqlens, inp.s_q, inp.h_q, inp.causal)[1]
 
@@ -102,7 +154,13 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter calibration) and exit")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="no GPU: write the workload's HBM bytes per decode launch to profiles/decode_traffic.json "
+                         "from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv outputs")
+    ap.add_argument("--copy-bytes", type=int, default=256 * 2 ** 20, help="size of the calibration copy")
     args = ap.parse_args(argv)
+    if args.pmc_summary:
+        return pmc_summary(args)
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
