@@ -3,21 +3,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload memory_bound]
 
 One step is one pass of the whole decode path over one synthetic batch:
-mla_get_metadata (split-KV plan) + mla_decode_fwd, issued as its two stages
-(decode kernel, split combine kernel) so that the decode kernel can be timed
-alone.
-W untimed steps, then K timed steps between device synchronisations. Each
-step reads a different replica of (kcache, block_table, q), and the replicas
-together exceed twice the 256 MB Infinity Cache, so the cache is read from
-HBM. Prints one JSON line.
+mla_get_metadata (split-KV plan) then mla_decode_fwd (decode kernel + split
+combine). Each step reads a different replica of (kcache, block_table, q), and
+the replicas together exceed twice the 256 MB Infinity Cache, so the cache is
+read from HBM. After W untimed steps, K steps captured in one HIP graph are replayed
+between two events on the launch stream.
+Prints one JSON line.
 
 value = algorithmic bytes per step / step time (GB/s); algorithmic bytes
 count each cached row once plus q, out, lse, the used block-table entries and
 cache_seqlens. tflops = (QK^T + PV MAC flops) / step time. The roofline entry
-is for the decode kernel alone: after the step timing, the same number of
-decode launches run back to back over the replicas between two events on
-their stream, and achieved = algorithmic bytes (or flops) per launch / the
-average launch time.
+is for the decode kernel alone: after the step timing, K decode-kernel launches
+(graphs holding only mla_decode_fwd_splits) run back to back over the replicas
+between two events on the same stream, and achieved = algorithmic bytes (or
+flops) per launch / the average launch time.
 """
 from __future__ import annotations
 
@@ -206,61 +205,69 @@ def main(argv=None):
     out = torch.empty((B, s_q, h_q, mla.D_V), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
     ws = torch.empty((sizes["workspace_bytes"],), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    plans = [(torch.empty((units, mla.META_INTS), dtype=torch.int32, device=dev),
+              torch.empty((B + 1,), dtype=torch.int32, device=dev)) for _ in range(R)]
 
-    def step(k, ev=None):
-        # plan, decode kernel, split combine: the same work as mla_get_metadata + mla_decode_fwd
+    def step(k):
+        # one pass of the path: the plan (mla_get_metadata), then mla_decode_fwd (decode kernel + combine)
         kc, q, tab, ln = reps[k % R]
-        meta, splits = mla.mla_get_metadata(ln, h_q, s_q, num_units=units)
-        if ev is not None:
-            ev[0].record(stream)
+        meta, splits = plans[k % R]
+        mla.mla_get_metadata(ln, h_q, s_q, num_units=units, tile_meta=meta, num_splits=splits)
+        mla.mla_decode_fwd(q, kc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal,
+                           out=out, lse=lse, workspace=ws)
+
+    def decode_only(k):
+        kc, q, tab, ln = reps[k % R]
+        meta, splits = plans[k % R]
         mla.mla_decode_fwd_splits(q, kc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal,
                                   out=out, lse=lse, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
-        mla.mla_combine_splits(splits, s_q, h_q, units, out, lse, ws)
-        if ev is not None:
-            ev[2].record(stream)
 
-    for k in range(args.warmup):
+    # The timed steps are captured in one HIP graph (step k uses replica k mod R) and replayed
+    # once, as a serving loop would run them: the host issues one launch for all K steps, so
+    # host-side argument marshalling stays out of the device timeline. The same steps issued
+    # eagerly are timed afterwards for reference (eager_ms_per_step).
+    for k in range(max(args.warmup, R)):
         step(k)
     torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
 
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        step(k, evs[k])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    dec_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    comb_avg = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for k in range(n):
+                fn(k)
+        torch.cuda.synchronize()
+        return g
 
-    # the decode kernel alone, launched back to back over the replicas: the
-    # roofline figure (per-launch event pairs inside the step add the launch
-    # latency of an isolated kernel, reported as kernel_ms_in_step)
-    kc0, q0, tab0, ln0 = reps[0]
-    meta0, splits0 = mla.mla_get_metadata(ln0, h_q, s_q, num_units=units)
-    for k in range(min(args.warmup, 5)):
-        kc, q, tab, ln = reps[k % R]
-        mla.mla_decode_fwd_splits(q, kc, tab, ln, inp.softmax_scale, meta0, splits0, causal=inp.causal,
-                                  out=out, lse=lse, workspace=ws)
-    k_start = torch.cuda.Event(enable_timing=True)
-    k_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    k_start.record(stream)
-    for k in range(args.steps):
-        kc, q, tab, ln = reps[k % R]
-        mla.mla_decode_fwd_splits(q, kc, tab, ln, inp.softmax_scale, meta0, splits0, causal=inp.causal,
-                                  out=out, lse=lse, workspace=ws)
-    k_end.record(stream)
-    torch.cuda.synchronize()
-    kern_ms = k_start.elapsed_time(k_end) / args.steps
+    def timed(run, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0.record(stream)
+        h0 = time.perf_counter()
+        run()
+        host = (time.perf_counter() - h0) * 1e3 / n
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, host
+
+    steps_graph = capture(step, args.steps)
+    if args.warmup:
+        capture(step, args.warmup).replay()
+    ms_step, host_ms = timed(steps_graph.replay, args.steps)
+    del steps_graph
+    # the decode kernel alone, K launches back to back over the replicas: the roofline figure
+    dec_graph = capture(decode_only, args.steps)
+    dec_graph.replay()
+    kern_ms, host_kern_ms = timed(dec_graph.replay, args.steps)
+    del dec_graph
+    n_eager = min(args.steps, 50)
+
+    def eager():
+        for k in range(n_eager):
+            step(k)
+    eager_ms, eager_host_ms = timed(eager, n_eager)
 
     value = nbytes / (ms_step * 1e-3) / 1e9
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -288,6 +295,9 @@ def main(argv=None):
         "tflops": round(tflops, 3),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+        "host_ms_per_step": round(host_ms, 6),
+        "eager_ms_per_step": round(eager_ms, 6),
+        "eager_host_ms_per_step": round(eager_host_ms, 6),
         "alg_bytes_per_step": nbytes,
         "alg_flops_per_step": flops,
         "roofline": {
@@ -299,10 +309,9 @@ def main(argv=None):
             "frac": round(k_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel_ms_avg": round(kern_ms, 6),
-            "kernel_ms_in_step": round(dec_avg, 6),
             "kernel_tflops": round(k_tf, 3),
             "kernel_mfma_frac": round(k_tf / BF16_PEAK_TFLOPS, 5),
-            "combine_ms_avg": round(comb_avg, 6),
+            "host_ms_per_launch": round(host_kern_ms, 6),
         },
     }
     if result["roofline"]["bound"] == "mfma":

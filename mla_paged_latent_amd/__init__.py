@@ -9,6 +9,7 @@ another implementation.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from pathlib import Path
 
@@ -88,6 +89,13 @@ def _stream(torch):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _on(torch, dev):
+    """Make dev the current device for the call (no-op when it already is)."""
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
+
+
 def _need(t, dtype, name, device=None):
     import torch
     if not isinstance(t, torch.Tensor):
@@ -106,19 +114,29 @@ def mla_workspace_bytes(batch: int, s_q: int, h_q: int, num_units: int) -> int:
     return workspace_bytes(batch, s_q, h_q, num_units)
 
 
-def mla_get_metadata(cache_seqlens, h_q: int, s_q: int = 1, num_units: int | None = None):
-    """Split-KV tile plan on the device. Returns (tile_meta int32 [G, 8], num_splits int32 [B+1])."""
+def mla_get_metadata(cache_seqlens, h_q: int, s_q: int = 1, num_units: int | None = None, tile_meta=None,
+                     num_splits=None):
+    """Split-KV tile plan on the device. Returns (tile_meta int32 [G, 8], num_splits int32 [B+1]);
+    pass tile_meta / num_splits to fill existing buffers."""
     import torch
     _need(cache_seqlens, torch.int32, "cache_seqlens")
     B = int(cache_seqlens.shape[0])
-    with torch.cuda.device(cache_seqlens.device):
+    dev = cache_seqlens.device
+    with _on(torch, dev):
         if num_units is None:
             num_units = mla_plan_sizes(B, s_q, h_q)["num_units"]
-        meta = torch.empty((num_units, META_INTS), dtype=torch.int32, device=cache_seqlens.device)
-        splits = torch.empty((B + 1,), dtype=torch.int32, device=cache_seqlens.device)
+        if tile_meta is None:
+            tile_meta = torch.empty((num_units, META_INTS), dtype=torch.int32, device=dev)
+        if num_splits is None:
+            num_splits = torch.empty((B + 1,), dtype=torch.int32, device=dev)
+        _need(tile_meta, torch.int32, "tile_meta", dev)
+        _need(num_splits, torch.int32, "num_splits", dev)
+        if tuple(tile_meta.shape) != (num_units, META_INTS) or tuple(num_splits.shape) != (B + 1,):
+            raise ValueError("tile_meta must be [num_units, 8] and num_splits [B + 1]")
         _check("mla_get_metadata", load_library().mla_get_metadata(
-            cache_seqlens.data_ptr(), B, s_q, h_q, num_units, meta.data_ptr(), splits.data_ptr(), _stream(torch)))
-    return meta, splits
+            cache_seqlens.data_ptr(), B, s_q, h_q, num_units, tile_meta.data_ptr(), num_splits.data_ptr(),
+            _stream(torch)))
+    return tile_meta, num_splits
 
 
 def mla_get_metadata_host(cache_seqlens, h_q: int, s_q: int, num_units: int):
@@ -177,7 +195,7 @@ def mla_decode_fwd(q, kcache, block_table, cache_seqlens, softmax_scale: float, 
     block_table int32 [B, max_blocks], cache_seqlens int32 [B].
     Returns (out bf16 [B, s_q, h_q, 512], lse float32 [B, s_q, h_q])."""
     import torch
-    with torch.cuda.device(q.device):
+    with _on(torch, q.device):
         args, out, lse, _ = _decode_args(q, kcache, block_table, cache_seqlens, softmax_scale, tile_meta,
                                          num_splits, causal, out, lse, workspace)
         _check("mla_decode_fwd", load_library().mla_decode_fwd(*args))
@@ -189,7 +207,7 @@ def mla_decode_fwd_splits(q, kcache, block_table, cache_seqlens, softmax_scale: 
     """First stage of mla_decode_fwd only (the decode kernel): unsplit sequences get
     out/lse, split ones leave partials in workspace. Returns (out, lse, workspace)."""
     import torch
-    with torch.cuda.device(q.device):
+    with _on(torch, q.device):
         args, out, lse, workspace = _decode_args(q, kcache, block_table, cache_seqlens, softmax_scale, tile_meta,
                                                  num_splits, causal, out, lse, workspace)
         _check("mla_decode_fwd_splits", load_library().mla_decode_fwd_splits(*args))
@@ -201,7 +219,7 @@ def mla_combine_splits(num_splits, s_q: int, h_q: int, num_units: int, out, lse,
     import torch
     _need(num_splits, torch.int32, "num_splits")
     B = int(num_splits.shape[0]) - 1
-    with torch.cuda.device(num_splits.device):
+    with _on(torch, num_splits.device):
         _check("mla_combine_splits", load_library().mla_combine_splits(
             num_splits.data_ptr(), B, s_q, h_q, num_units, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
             int(workspace.numel()), _stream(torch)))

@@ -121,23 +121,39 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
         copy_rows(gbase, min(16, tok_end - tok), slot0 + (unsigned)(k & 1) * kSlotA, 0, 1, kDmaA, lane);
     };
 
+    // Prologue. Every wave's first slot is issued first; the workgroup's 16
+    // query rows are copied to LDS (into wave 3's second slot, padded rows like
+    // the cache slots) by all four waves, so that no compiler-visible load has
+    // to be awaited behind the block copies: each wave can start on its first
+    // slot while its second is still in flight.
+    static_assert(NR == 1, "one 16-row query tile per workgroup");
+    const unsigned qslot = lds0 + 7u * kSlotA;
+    const unsigned char* qbase = (const unsigned char*)(p.q + ((size_t)b * p.rows_total + blockIdx.y * R) * kDqk);
+    settle_loads();                                         // page_vec: every later wait is for copies only
     if (K > 0) issue(0);
-    if (K > 1) issue(1);
-
-    // queries (issued after the first copies; the settle below waits for both)
+    copy_rows(qbase, R, qslot, wave, 4, kDmaA, lane);
+    if (wave < 3 && K > 1) {
+        issue(1);
+        MLA_WAIT_VM(19);                                   // the slot-0 and query copies have landed
+    } else {
+        MLA_WAIT_VM(0);
+    }
+    wg_barrier();
     bf16x8 qf[NR][18];
+    {
+        const unsigned qa = qslot + (unsigned)(c16 * kLdsRow + 16 * g);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) qf[0][ks] = __builtin_bit_cast(bf16x8, lds_load16(qa + 64 * ks));
+    }
+    wg_barrier();                                           // every wave holds its queries
+    if (wave == 3 && K > 1) issue(1);
     int lim[NR];
 #pragma unroll
     for (int rt = 0; rt < NR; ++rt) {
         const int row = blockIdx.y * R + rt * 16 + c16;
-        const uint16_t* qrow = p.q + ((size_t)b * p.rows_total + row) * kDqk + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, *(const s16x8*)(qrow + 32 * ks));
         const int iq = row / p.h_q;
         lim[rt] = min(tok_end, p.causal ? L - (p.s_q - 1 - iq) : L);
     }
-    settle_loads();
-
 
     const unsigned a_off = (unsigned)(token_of_row(c16) * kLdsRow + g * 16);
     const unsigned v_off = (unsigned)(token_of_row(4 * g + (c16 >> 2)) * kLdsRow + 8 * (c16 & 3));
@@ -154,6 +170,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
         s16x4 va[32];
 #pragma unroll
         for (int nt = 0; nt < 32; ++nt) va[nt] = lds_tr4(sb + v_off + 32 * nt);
+        // the slot's reads are done: refill it with sub-tile k + 2
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (k + 2 < K) issue(k + 2);
 
         // S^T = K Q^T for 16 tokens x R rows, two accumulation chains
         f32x4 s[NR];
@@ -167,10 +186,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
             }
             s[rt] = e0 + e1;
         }
-
-        // the slot's reads are done: refill it with sub-tile k + 2
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (k + 2 < K) issue(k + 2);
 
         // scale, mask, online softmax; s[rt][i] is token tok0 + token_of_row(4g + i)
         s16x4 pb[NR];
@@ -188,20 +203,20 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
             const bool need = tmax > mrun[rt] + kLazyTau;
             if (wave_any(need)) {
                 const float mnew = need ? tmax : mrun[rt];
-                const float alpha = need ? exp2f(mrun[rt] - mnew) : 1.f;
+                const float alpha = need ? __builtin_amdgcn_exp2f(mrun[rt] - mnew) : 1.f;
                 lrun[rt] *= alpha;
 #pragma unroll
                 for (int nt = 0; nt < 32; ++nt) acc[rt][nt] *= alpha;
                 mrun[rt] = mnew;
             }
             const float muse = mrun[rt] == -INFINITY ? 0.f : mrun[rt];
-            float psum = 0.f;
+            float pv[4], psum = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pv = exp2f(s[rt][i] - muse);
-                psum += pv;
-                pb[rt][i] = (short)bf16_rne(pv);
+                pv[i] = __builtin_amdgcn_exp2f(s[rt][i] - muse);
+                psum += pv[i];
             }
+            pb[rt] = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])});
             lrun[rt] += xor32_sum(xor16_sum(psum));
         }
 
@@ -215,67 +230,58 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
 
     // ---- merge the four waves' (m, l, O) and write the result. Wave w owns
     // output tiles nt in [8w, 8w + 8) (dims [128w, 128w + 128)) and keeps them
-    // in registers; it posts its other 24 tiles to LDS as bf16 (unscaled) for
-    // their owners, and its running max/sum for every row.
-    wg_barrier();                                            // every wave is done with its slots
-    lds_f32* stat_m = (lds_f32*)(uintptr_t)lds0;            // [4][R]
-    lds_f32* stat_l = stat_m + 4 * R;                         // [4][R]
-    const unsigned xbuf = lds0 + 1024;                       // [4][NR][32 tiles][64 lanes] x 8 B
-    if (g == 0) {
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            stat_m[wave * R + rt * 16 + c16] = mrun[rt];
-            stat_l[wave * R + rt * 16 + c16] = lrun[rt];
+    // in registers. As soon as it is done with its slots it posts its other 24
+    // tiles (unscaled, bf16) and its running max/sum per row into its own slot
+    // area; one workgroup barrier later every wave folds in the others' tiles.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");       // this wave's slot reads are done
+    {
+        const unsigned mine = slot0;
+        if (g == 0) {
+            *(lds_f32*)(uintptr_t)(mine + 16384u + 4u * c16) = mrun[0];
+            *(lds_f32*)(uintptr_t)(mine + 16384u + 64u + 4u * c16) = lrun[0];
         }
-    }
-#pragma unroll
-    for (int rt = 0; rt < NR; ++rt)
 #pragma unroll
         for (int nt = 0; nt < 32; ++nt) {
             if ((nt >> 3) == wave) continue;
-            s16x4 v;
-            v[0] = (short)bf16_rne(acc[rt][nt][0]);
-            v[1] = (short)bf16_rne(acc[rt][nt][1]);
-            v[2] = (short)bf16_rne(acc[rt][nt][2]);
-            v[3] = (short)bf16_rne(acc[rt][nt][3]);
-            *(lds_s16x4_rw*)(uintptr_t)(xbuf + (unsigned)((((wave * NR + rt) * 32 + nt) * 64 + lane) * 8)) = v;
+            const u32x2 v = {pack_bf16x2(acc[0][nt][0], acc[0][nt][1]), pack_bf16x2(acc[0][nt][2], acc[0][nt][3])};
+            *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(mine + (unsigned)((nt * 64 + lane) * 8)) = v;
         }
+    }
     wg_barrier();
-#pragma unroll
-    for (int rt = 0; rt < NR; ++rt) {
-        const int rrow = rt * 16 + c16;
+    {
         float mw[4], mall = -INFINITY;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            mw[w] = stat_m[w * R + rrow];
+            mw[w] = *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 4u * c16);
             mall = fmaxf(mall, mw[w]);
         }
         float fw[4], lt = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            fw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - mall);
-            lt += stat_l[w * R + rrow] * fw[w];
+            fw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mall);
+            lt += *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 64u + 4u * c16) * fw[w];
         }
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int grow = blockIdx.y * R + rrow;
+        const int grow = blockIdx.y * R + c16;
 #pragma unroll
         for (int nt = 0; nt < 32; ++nt) {
             if ((nt >> 3) != wave) continue;                  // static tile index, uniform branch
-            f32x4 v = acc[rt][nt] * fw[nt >> 3];
+            f32x4 v = acc[0][nt] * fw[nt >> 3];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 if (w == wave) continue;
-                const s16x4 o = *(const lds_s16x4_rw*)(uintptr_t)(
-                    xbuf + (unsigned)((((w * NR + rt) * 32 + nt) * 64 + lane) * 8));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] += __uint_as_float((unsigned)(unsigned short)o[i] << 16) * fw[w];
+                const u32x2 o = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(
+                    lds0 + (unsigned)(2 * w) * kSlotA + (unsigned)((nt * 64 + lane) * 8));
+                v[0] += __uint_as_float(o[0] << 16) * fw[w];
+                v[1] += __uint_as_float(o[0] & 0xFFFF0000u) * fw[w];
+                v[2] += __uint_as_float(o[1] << 16) * fw[w];
+                v[3] += __uint_as_float(o[1] & 0xFFFF0000u) * fw[w];
             }
             v *= inv;
             const int d = 16 * nt + 4 * g;
             if (nsplit == 1) {
-                ushort4 ob;
-                ob.x = bf16_rne(v[0]); ob.y = bf16_rne(v[1]); ob.z = bf16_rne(v[2]); ob.w = bf16_rne(v[3]);
-                *(ushort4*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = ob;
+                const u32x2 ob = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                *(u32x2*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = ob;
             } else {
                 *(f32x4*)(p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d) = v;
             }
@@ -292,11 +298,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
 
 // Merge split partials by their log-sum-exp: out = sum_k exp(lse_k - L) o_k,
 // lse = L = log sum_k exp(lse_k). One thread per 4 dims of one (sequence, row);
-// sequences with no block get out = 0, lse = -inf; unsplit ones were written by
-// the decode kernel.
+// the partials are read U at a time (their lse and o loads issued together)
+// and folded in with a running max. Sequences with no block get out = 0,
+// lse = -inf; unsplit ones were written by the decode kernel.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
 {
-    constexpr int U = 8;                                    // partials in flight per thread
+    constexpr int U = 16;                                   // partials in flight per thread
     const int t = threadIdx.x & 127;                        // 4-dim chunk of the row
     const int row = blockIdx.x * 2 + (threadIdx.x >> 7);
     const int b = blockIdx.y;
@@ -307,46 +314,47 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
     uint16_t* o = p.out + ((size_t)b * p.rows_total + row) * kDv + 4 * t;
     float* lo = p.lse + (size_t)b * p.rows_total + row;
     const float* lse_col = p.part_lse + (size_t)s0 * p.rows_total + row;
-    float mx = -INFINITY;
+    const float* o_col = p.part_o + ((size_t)s0 * p.rows_total + row) * kDv + 4 * t;
+    float m = -INFINITY, l = 0.f;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < ns; k += U) {
         float w[U];
+        f32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) w[u] = (k + u < ns) ? lse_col[(size_t)(k + u) * p.rows_total] : -INFINITY;
+        for (int u = 0; u < U; ++u) {
+            w[u] = -INFINITY;
+            v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (k + u < ns) {
+                w[u] = lse_col[(size_t)(k + u) * p.rows_total];
+                v[u] = *(const f32x4*)(o_col + (size_t)(k + u) * p.rows_total * kDv);
+            }
+        }
+        float mk = m;
 #pragma unroll
-        for (int u = 0; u < U; ++u) mx = fmaxf(mx, w[u]);
+        for (int u = 0; u < U; ++u) mk = fmaxf(mk, w[u]);
+        if (mk == -INFINITY) continue;                      // nothing visible yet
+        const float sc = __expf(m - mk);                    // 0 while m is -inf
+        l *= sc;
+        a *= sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float e = __expf(w[u] - mk);
+            l += e;
+            a += v[u] * e;
+        }
+        m = mk;
     }
-    if (ns == 0 || mx == -INFINITY) {
+    if (m == -INFINITY) {
         *(ushort4*)o = make_ushort4(0, 0, 0, 0);
         if (t == 0) *lo = -INFINITY;
         return;
     }
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    const float* o_col = p.part_o + ((size_t)s0 * p.rows_total + row) * kDv + 4 * t;
-    for (int k = 0; k < ns; k += U) {
-        f32x4 v[U];
-        float w[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool ok = k + u < ns;
-            w[u] = ok ? lse_col[(size_t)(k + u) * p.rows_total] : -INFINITY;
-            v[u] = ok ? *(const f32x4*)(o_col + (size_t)(k + u) * p.rows_total * kDv) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float e = __expf(w[u] - mx);
-            wsum += e;
-            a += v[u] * e;
-        }
-    }
-    const float inv = 1.f / wsum;
-    ushort4 r;
-    r.x = bf16_rne(a[0] * inv);
-    r.y = bf16_rne(a[1] * inv);
-    r.z = bf16_rne(a[2] * inv);
-    r.w = bf16_rne(a[3] * inv);
-    *(ushort4*)o = r;
-    if (t == 0) *lo = mx + __logf(wsum);
+    const float inv = 1.f / l;
+    u32x2 r;
+    r[0] = pack_bf16x2(a[0] * inv, a[1] * inv);
+    r[1] = pack_bf16x2(a[2] * inv, a[3] * inv);
+    *(u32x2*)o = r;
+    if (t == 0) *lo = m + __logf(l);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream)

@@ -35,7 +35,7 @@ __device__ __forceinline__ Segment unit_segment(const DecodeParams& p, int b, in
 {
     Segment s;
     s.b = b;
-    s.L = sload(p.seqlens + b);
+    s.L = cload(p.seqlens + b);
     const int nb = blocks_of(s.L);
     s.tb = (b == b0 ? j0 : 0) * kPage;
     const int je = (b == b1) ? j1 : nb;
@@ -86,8 +86,8 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     Segment is = next_segment(p, b0, b0, j0, b1, j1);      // copy cursor
     if (is.b >= p.batch) return;
     int itok = is.tb;
-    int ipage_idx = -1;
-    const unsigned char* ipage = nullptr;
+    // page of the next slot to copy, loaded one slot ahead of its use
+    int ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
     Segment cs = is;                                        // compute cursor
 
     // This wave's 9 copies of a slot: copy i = wave + 4k, lane l fills LDS
@@ -102,44 +102,50 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
         dma_off[k] = (unsigned)(r * kRowBytes + (((q - r * kChunks) ^ (r & 7)) << 4));
     }
     int n_issued = 0;
-    auto issue = [&]() {
-        const int pidx = itok >> 6;
-        if (pidx != ipage_idx) {
-            const int pg = sload(p.block_table + (size_t)is.b * p.max_blocks + pidx);
-            ipage = (const unsigned char*)p.kcache + (size_t)pg * kPageBytes;
-            ipage_idx = pidx;
-        }
-        const unsigned char* gbase = ipage + (size_t)(itok & 63) * kRowBytes;
-        const int valid = is.te - itok;
-        const unsigned slot = lds0 + (unsigned)(n_issued & 3) * kSlotB + (unsigned)wave * 1024u;
-        if (valid >= 32) {
-#pragma unroll
-            for (int k = 0; k < 9; ++k) dma16s(gbase, dma_off[k], slot + 4096u * k);
-        } else {
-            // rows past the end are copied from row 0 (finite data, masked later)
-#pragma unroll
-            for (int k = 0; k < 9; ++k)
-                dma16s(gbase, dma_row[k] < valid ? dma_off[k] : dma_off[k] - (unsigned)(dma_row[k] * kRowBytes),
-                       slot + 4096u * k);
-        }
+    // The next slot to copy: global base, LDS base of this wave's copies, and
+    // how many of its 32 rows are real (rows past the end are copied from row
+    // 0: finite data, masked later).
+    struct Copy {
+        const unsigned char* gbase;
+        unsigned slot;
+        int valid;
+    };
+    auto copy_begin = [&]() {
+        Copy cp;
+        cp.gbase = (const unsigned char*)p.kcache + (size_t)ipage * kPageBytes + (size_t)(itok & 63) * kRowBytes;
+        cp.slot = lds0 + (unsigned)(n_issued & 3) * kSlotB + (unsigned)wave * 1024u;
+        cp.valid = is.te - itok;
+        return cp;
+    };
+    auto copy_one = [&](const Copy& cp, int k) {
+        const unsigned off = cp.valid >= 32 || dma_row[k] < cp.valid ? dma_off[k]
+                                                                     : dma_off[k] - (unsigned)(dma_row[k] * kRowBytes);
+        dma16s(cp.gbase, off, cp.slot + 4096u * k);
+    };
+    auto copy_end = [&]() {
         ++n_issued;
         itok += 32;
         if (itok >= is.te) {
             is = next_segment(p, is.b + 1, b0, j0, b1, j1);
             itok = is.tb;
-            ipage_idx = -1;
         }
+        if (is.b < p.batch && (itok & 63) == 0) ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
+    };
+    auto issue = [&]() {
+        const Copy cp = copy_begin();
+#pragma unroll
+        for (int k = 0; k < 9; ++k) copy_one(cp, k);
+        copy_end();
     };
     // wait until slot m has landed (for this wave's copies), then sync the
-    // workgroup; afterwards refill the ring while slot `oldest` stays untouched
-    auto arrive = [&](int m, int oldest) {
+    // workgroup; the ring may then be refilled while slot `oldest` stays untouched
+    auto arrive = [&](int m) {
         const int later = n_issued - 1 - m;
         if (later <= 0) MLA_WAIT_VM(0);
         else if (later == 1) MLA_WAIT_VM(9);
         else if (later == 2) MLA_WAIT_VM(18);
         else MLA_WAIT_VM(27);
         wg_barrier();
-        while (is.b < p.batch && n_issued < oldest + 4) issue();
     };
     for (int k = 0; k < 3 && is.b < p.batch; ++k) issue();
 
@@ -213,7 +219,10 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
         };
         // the same, with the exponentials of the previous slot's softmax placed
         // between the matrix ops (they are independent of them)
-        auto qk_exp = [&](int m, const float* sv, float muse, float* pv) {
+        // (and, when `copy` is set, this wave's nine copies of the next ring
+        // slot spread over the matrix ops, so their issue never stalls the
+        // wave for long)
+        auto qk_exp = [&](int m, const float* sv, float cs, float muse, float* pv, bool copy, const Copy& cp) {
             const unsigned sb = lds0 + (unsigned)(m & 3) * kSlotB;
             f32x16 s;
 #pragma unroll
@@ -226,7 +235,8 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
                 __builtin_amdgcn_sched_barrier(0);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv[ks & 3]), qf[ks], s, 0, 0, 0);
                 if (ks + 4 < 18) kv[ks & 3] = load_k(sb, ks + 4);
-                if (ks < 16) pv[ks] = __builtin_amdgcn_exp2f(sv[ks] - muse);
+                if (ks < 16) pv[ks] = __builtin_amdgcn_exp2f(fmaf(sv[ks], cs, -muse));
+                if ((ks & 1) && copy) copy_one(cp, ks >> 1);
             }
             __builtin_amdgcn_sched_barrier(0);
             return s;
@@ -248,20 +258,27 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
         // element i is token t0 + token_of_row(8(i/4) + 4h + i%4) of query row
         // r32. Scales and masks the scores into sv, raises the running max
         // (rescaling O and the sum) and returns the max the exponentials use.
-        auto prepare = [&](const f32x16& s, int t0, float* sv) {
-            if (t0 + 32 <= lim_lo) {
+        // Without masking (and with a positive scale) sv keeps the raw scores
+        // and `cs` returns the scale; with masking sv holds scaled, masked
+        // scores and cs = 1. The exponentials take exp2(sv * cs - max).
+        auto prepare = [&](const f32x16& s, int t0, float* sv, float& cs) {
+            float m4[4];
+            if (t0 + 32 <= lim_lo && c > 0.f) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sv[i] = s[i] * c;
+                for (int i = 0; i < 16; ++i) sv[i] = s[i];
+                cs = c;
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int t = t0 + token_of_row(8 * (i >> 2) + 4 * h + (i & 3));
                     sv[i] = (t < lim) ? s[i] * c : -INFINITY;
                 }
+                cs = 1.f;
             }
-            float tmax = sv[0];
 #pragma unroll
-            for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sv[i]);
+            for (int j = 0; j < 4; ++j)
+                m4[j] = fmaxf(fmaxf(sv[4 * j], sv[4 * j + 1]), fmaxf(sv[4 * j + 2], sv[4 * j + 3]));
+            float tmax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * cs;   // the scaled max (cs > 0)
             tmax = xor32_max(tmax);
             const bool need = tmax > mrun + kLazyTau;
             if (wave_any(need)) {
@@ -276,10 +293,10 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
         };
         // second half: row sums and P^T as the bf16 B operands of the two PV k-steps
         auto finish = [&](const float* pv, bf16x8* pb) {
-            float psum = 0.f;
+            float q4[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) psum += pv[i];
-            lrun += xor32_sum(psum);
+            for (int j = 0; j < 4; ++j) q4[j] = (pv[4 * j] + pv[4 * j + 1]) + (pv[4 * j + 2] + pv[4 * j + 3]);
+            lrun += xor32_sum((q4[0] + q4[1]) + (q4[2] + q4[3]));
 #pragma unroll
             for (int kp = 0; kp < 2; ++kp) {
                 u32x4 w;
@@ -315,19 +332,24 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
 
         // first slot of the segment; afterwards each step issues the next
         // slot's QK^T beside this slot's exponentials, then this slot's PV
-        arrive(n, n);
+        arrive(n);
+        while (is.b < p.batch && n_issued < n + 4) issue();
         f32x16 s = exchange(qk(n));
         for (int t0 = cs.tb;; t0 += 32) {
             const bool more = t0 + 32 < cs.te;
-            float sv[16], pv[16];
-            const float muse = prepare(s, t0, sv);
+            float sv[16], pv[16], scl;
+            const float muse = prepare(s, t0, sv, scl);
             f32x16 s_next;
             if (more) {
-                arrive(n + 1, n);
-                s_next = qk_exp(n + 1, sv, muse, pv);
+                arrive(n + 1);
+                // slot n is still read by this step's PV: refill only up to n + 3
+                const bool copy = is.b < p.batch && n_issued < n + 4;
+                const Copy cp = copy_begin();
+                s_next = qk_exp(n + 1, sv, scl, muse, pv, copy, cp);
+                if (copy) copy_end();
             } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(sv[i] - muse);
+                for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], scl, -muse));
             }
             bf16x8 pb[2];
             finish(pv, pb);

@@ -74,6 +74,15 @@ __device__ __forceinline__ int sload(const int32_t* ptr)
     return v;
 }
 
+// Load of a wave-uniform int through the constant address space: the
+// compiler emits a scalar load counted by lgkmcnt and waits for it only where
+// the value is first used, so it can be issued well ahead of that use. Only
+// for buffers that no one writes while the kernel runs.
+__device__ __forceinline__ int cload(const int32_t* ptr)
+{
+    return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)ptr;
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Scalar load of 8 consecutive wave-uniform ints (one plan row).

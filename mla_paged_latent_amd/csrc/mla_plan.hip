@@ -16,24 +16,36 @@ namespace mla {
 
 constexpr int kPlanThreads = 1024;
 
-// Inclusive prefix sum of a[0..n) in LDS by one workgroup of kPlanThreads.
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int x)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Inclusive prefix sum of a[0..n) in LDS by one workgroup of kPlanThreads:
+// every thread sums a contiguous chunk, the chunk sums are scanned within each
+// wave and across the waves' totals (carry[], one int per wave), then every
+// thread rewrites its chunk. Two workgroup barriers.
 __device__ void block_inclusive_scan(int* a, int n, int* carry)
 {
     const int tid = threadIdx.x;
+    const int wave = tid >> 6;
     const int per = (n + kPlanThreads - 1) / kPlanThreads;
     const int lo = tid * per;
     const int hi = min(lo + per, n);
     int local = 0;
     for (int k = lo; k < hi; ++k) local += a[k];
-    carry[tid] = local;
+    const int incl = wave_inclusive_scan(local);
+    if ((tid & 63) == 63) carry[wave] = incl;
     __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        int v = (tid >= off) ? carry[tid - off] : 0;
-        __syncthreads();
-        carry[tid] += v;
-        __syncthreads();
-    }
-    int run = carry[tid] - local;
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += carry[w];
     for (int k = lo; k < hi; ++k) {
         run += a[k];
         a[k] = run;
@@ -61,7 +73,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     extern __shared__ int plan_smem[];
     int* P = plan_smem;                  // [batch + 1]
     int* NS = P + (batch + 1);           // [batch + 1]
-    int* carry = NS + (batch + 1);       // [kPlanThreads]
+    int* carry = NS + (batch + 1);       // [kPlanThreads / 64]
     const int tid = threadIdx.x;
 
     if (plan_by_sequence(rows_wg)) {
@@ -167,7 +179,7 @@ void plan_host(const int32_t* seqlens, int batch, int rows_wg, int num_units, in
 hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_units, int32_t* meta,
                        int32_t* splits, hipStream_t stream)
 {
-    size_t lds = sizeof(int) * (2 * (size_t)(batch + 1) + kPlanThreads);
+    size_t lds = sizeof(int) * (2 * (size_t)(batch + 1) + kPlanThreads / 64);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds);

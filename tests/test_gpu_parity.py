@@ -188,3 +188,45 @@ def test_device_plan_large_batch(h_q, units):
     dmeta, dsplits = mla.mla_get_metadata(torch.from_numpy(lens).cuda(), h_q, 1, num_units=units)
     hmeta, hsplits = mla.mla_get_metadata_host(lens, h_q, 1, units)
     assert np.array_equal(dmeta.cpu().numpy(), hmeta) and np.array_equal(dsplits.cpu().numpy(), hsplits)
+
+
+# ------------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("lens,s_q,h_q", [([700, 65, 3000, 1], 1, 16), ([300, 2000, 64], 2, 128)])
+def test_graph_replays_match_eager(lens, s_q, h_q):
+    """The plan + decode captured in a HIP graph (as the benchmark times it) gives, on every
+    replay, exactly the eager result; eager work and synchronisations run between replays."""
+    _say("graph capture lens=%s s_q=%d h_q=%d" % (lens, s_q, h_q))
+    inp = cases.small_batch(lens, s_q=s_q, h_q=h_q, seed=sum(lens) + 7)
+    dev = to_device(inp)
+    B = len(lens)
+    units = mla.mla_plan_sizes(B, s_q, h_q)["num_units"]
+    meta = torch.empty((units, mla.META_INTS), dtype=torch.int32, device="cuda:0")
+    splits = torch.empty((B + 1,), dtype=torch.int32, device="cuda:0")
+    out = torch.empty((B, s_q, h_q, mla.D_V), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty((mla.workspace_bytes(B, s_q, h_q, units),), dtype=torch.uint8, device="cuda:0")
+
+    def run():
+        mla.mla_get_metadata(dev["cache_seqlens"], h_q, s_q, num_units=units, tile_meta=meta, num_splits=splits)
+        mla.mla_decode_fwd(dev["q"], dev["kcache"], dev["block_table"], dev["cache_seqlens"], inp.softmax_scale,
+                           meta, splits, causal=inp.causal, out=out, lse=lse, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        run()
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        meta.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), "replay %d differs" % rep
+        run()                       # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o), "eager run after replay %d differs" % rep
+    ref_out, ref_lse = _oracle(inp)
+    assert_parity(out.float().cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, "graph")

@@ -104,6 +104,8 @@ def test_plan_sizes(lib):
     # 64 query rows per workgroup: h_q=128, s_q=2 is 256 rows = four head groups
     assert mla.mla_plan_sizes(128, 2, 128, num_cus=256)["num_units"] == 64
     assert mla.mla_plan_sizes(64, 1, 128, num_cus=256)["num_units"] == 128
+    # 192 rows = three head groups
+    assert mla.mla_plan_sizes(64, 3, 64, num_cus=256)["num_units"] == 85
     assert mla.mla_plan_sizes(64, 1, 64, num_cus=256)["num_units"] == 256
     # 48 rows: three head groups of 16, per-sequence plan
     assert mla.mla_plan_sizes(8, 3, 16, num_cus=256)["num_units"] == 85
