@@ -114,18 +114,34 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
         goff[k] = (unsigned)(r * kRowBytes + (((q - r * kChunks) ^ (r & 7)) << 4));
     }
     int n_issued = 0;
-    // Copy the next block of the copy cursor into LDS block (n_issued % 2).
-    // Rows past the segment's end are copied from the block's first row
-    // (finite data, masked to p = 0).
+    // The next block of the copy cursor goes to LDS block (n_issued % 2):
+    // copy_src / copy_dst give the global page and this wave's LDS base.
+    auto copy_src = [&]() { return (const unsigned char*)p.kcache + (size_t)ipage * kPageBytes; };
+    auto copy_dst = [&]() { return lds0 + (unsigned)(n_issued & 1) * kBlockB + (unsigned)wave * 1024u; };
+    // copy k (0..17) of a whole block: half k / 9, copy k % 9 of that half
+    auto copy_full = [&](const unsigned char* gbase, unsigned dst, int k) {
+        const unsigned hb = k < 9 ? 0u : (unsigned)kHalfB;
+        dma16s(gbase, goff[k % 9] + hb, dst + hb + 4096u * (unsigned)(k % 9));
+    };
+    // advance the copy cursor past the block just copied
+    auto copy_end = [&]() {
+        ++n_issued;
+        itok += kPage;
+        if (itok >= is.te) {
+            is = next_segment(p, is.b + 1, b0, j0, b1, j1);
+            itok = is.tb;
+        }
+        if (is.b < p.batch) ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
+    };
+    // Copy the next block all at once. Rows past the segment's end are copied
+    // from the block's first row (finite data, masked to p = 0).
     auto issue = [&]() {
-        const unsigned char* gbase = (const unsigned char*)p.kcache + (size_t)ipage * kPageBytes;
-        const unsigned dst = lds0 + (unsigned)(n_issued & 1) * kBlockB + (unsigned)wave * 1024u;
+        const unsigned char* gbase = copy_src();
+        const unsigned dst = copy_dst();
         const int valid = is.te - itok;
         if (valid >= kPage) {
 #pragma unroll
-            for (int k = 0; k < 9; ++k) dma16s(gbase, goff[k], dst + 4096u * k);
-#pragma unroll
-            for (int k = 0; k < 9; ++k) dma16s(gbase, goff[k] + (unsigned)kHalfB, dst + (unsigned)kHalfB + 4096u * k);
+            for (int k = 0; k < 18; ++k) copy_full(gbase, dst, k);
         } else {
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb)
@@ -138,13 +154,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
                     dma16s(gbase, src, dst + (unsigned)(hb * kHalfB) + 4096u * k);
                 }
         }
-        ++n_issued;
-        itok += kPage;
-        if (itok >= is.te) {
-            is = next_segment(p, is.b + 1, b0, j0, b1, j1);
-            itok = is.tb;
-        }
-        if (is.b < p.batch) ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
+        copy_end();
     };
     issue();
 
@@ -204,15 +214,22 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
             // LDS block takes the next copy
             MLA_WAIT_VM(0);
             wg_barrier();
-            if (is.b < p.batch) issue();
+            // The next block (into the LDS block that block n - 1 just left):
+            // a whole one is copied during the QK^T below, one copy per pair of
+            // matrix ops, so that the waits of the copy issue overlap the matrix
+            // work; a partial one (the end of a segment) is copied here.
+            const bool spread = is.b < p.batch && is.te - itok >= kPage;
+            if (is.b < p.batch && !spread) issue();
             const unsigned blk = lds0 + (unsigned)(n & 1) * kBlockB;
 
             // ---- partial S^T over this wave's column half: s0 owned row group, s1 the other
             f32x16 s0, s1;
 #pragma unroll
             for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-            {
+            auto qk = [&](auto with_copy) {
                 const unsigned sb = blk + (unsigned)th * kHalfB;
+                const unsigned char* gbase = copy_src();
+                const unsigned dst = copy_dst();
                 s16x8 kv[4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) kv[ks] = lds_load16(sb + k_off[ks & 3] + 128u * (unsigned)(ks >> 2));
@@ -223,8 +240,15 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
                     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][ks], s0, 0, 0, 0);
                     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][ks], s1, 0, 0, 0);
                     if (ks + 4 < 18) kv[ks & 3] = lds_load16(sb + k_off[(ks + 4) & 3] + 128u * (unsigned)((ks + 4) >> 2));
+                    if constexpr (decltype(with_copy)::value) copy_full(gbase, dst, ks);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+            };
+            if (spread) {
+                qk(std::true_type{});
+                copy_end();
+            } else {
+                qk(std::false_type{});
             }
             // ---- score exchange: send the partner's row group (s1), add the partner's half of mine (s0)
             f32x16 s = s0;
