@@ -142,6 +142,73 @@ def inp_flops(inp):
     return wl.algorithmic_counts(inp.cache_seqlens, inp.s_q, inp.h_q, inp.causal)[1]
 
 
+def bench_append(args, torch, mla, dev):
+    """The cache append alone (mla_append_kv): K launches over replicas of (cache, new rows)."""
+    inp = wl.make_append()
+    nbytes = wl.append_bytes(inp)
+    rep_bytes = inp.kcache.nbytes + inp.new_rows.nbytes
+    R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / rep_bytes))
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    table = torch.from_numpy(inp.block_table).to(dev)
+    lens = torch.from_numpy(inp.cache_seqlens).to(dev)
+    reps = [(bf16(inp.kcache), bf16(inp.new_rows)) for _ in range(R)]
+
+    def step(k):
+        kc, rows = reps[k % R]
+        mla.mla_append_kv(kc, table, lens, rows)
+
+    for k in range(max(args.warmup, R)):
+        step(k)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for k in range(args.steps):
+            step(k)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    B, s_new = inp.new_rows.shape[:2]
+    result = {
+        "metric": "MLA cache append HBM GB/s (fraction of MI355X peak), paged bf16",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "append: " + wl.APPEND_DESCRIPTION + ", row 576 bf16, block 64, shuffled block_table",
+                   "batch": int(B), "s_new": int(s_new), "replicas": R},
+        "alg_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "append_kernel (mla_append_kv)", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_ms_avg": round(ms, 6)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import append as oracle_append
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            oracle_append.append_rows(inp.kcache, inp.block_table, inp.cache_seqlens, inp.new_rows)
+            n += 1
+            if time.perf_counter() - t0 >= min(args.cpu_seconds, 10.0) or n >= 50:
+                break
+        sec = (time.perf_counter() - t0) / n
+        result["cpu_baseline"] = {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": "%d full appends of the workload (copy of the cache included)" % n}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +224,8 @@ def main(argv=None):
                     help="no GPU: write the workload's HBM bytes per decode launch to profiles/decode_traffic.json "
                          "from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv outputs")
     ap.add_argument("--copy-bytes", type=int, default=256 * 2 ** 20, help="size of the calibration copy")
+    ap.add_argument("--op", default="decode", choices=["decode", "append"],
+                    help="decode: the hot path (default); append: the cache-append kernel alone")
     args = ap.parse_args(argv)
     if args.pmc_summary:
         return pmc_summary(args)
@@ -185,6 +254,8 @@ def main(argv=None):
         return 0
 
     mla.load_library()
+    if args.op == "append":
+        return bench_append(args, torch, mla, dev)
     inp = wl.make_workload(args.workload, poison=False)
     B, s_q, h_q = inp.batch, inp.s_q, inp.h_q
     nbytes, flops = wl.algorithmic_counts(inp.cache_seqlens, s_q, h_q, inp.causal)

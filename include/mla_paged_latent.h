@@ -62,7 +62,9 @@ typedef enum mla_status {
     MLA_ERR_INVALID_ARG = -1,         /* null pointer, non-positive size, bad alignment */
     MLA_ERR_UNSUPPORTED = -2,         /* shape the kernels do not handle (s_q*h_q) */
     MLA_ERR_WORKSPACE_TOO_SMALL = -3,
-    MLA_ERR_HIP = -4                  /* a HIP runtime call or launch failed */
+    MLA_ERR_HIP = -4,                 /* a HIP runtime call or launch failed */
+    MLA_ERR_OUT_OF_BLOCKS = -5,       /* block pool: not enough free blocks (nothing changed) */
+    MLA_ERR_OUT_OF_MEMORY = -6        /* block pool: host allocation failed (nothing changed) */
 } mla_status;
 
 /* Human-readable text for a status code. Never NULL. */
@@ -175,6 +177,65 @@ int mla_decode_fwd_splits(const void* q, const void* kcache, int64_t nblocks,
 
 int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, int num_units,
                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Cache append: writes the new tokens' cached rows into their blocks, the
+ * step that precedes decode attention over them (the cache grows by the new
+ * tokens' entries each step: "OpenSourceWeek Day 1: FlashMLA", "How KV
+ * Caching Works?"; blocks found through the block table: FlashMLA
+ * explainer, section 4.3.2 "Paged KV Cache").
+ *   kcache: device bf16 [nblocks, 64, 576], 16-byte aligned; written only at
+ *     the new rows' positions.
+ *   block_table: device int32 [batch, max_blocks].
+ *   cache_seqlens: device int32 [batch], lengths INCLUDING the new tokens
+ *     (the same array mla_decode_fwd then takes).
+ *   new_rows: device bf16 [batch, s_new, 576], 16-byte aligned. Row i of
+ *     sequence b goes to token position L_b - s_new + i (so the new tokens are
+ *     the last s_new positions, as mla_decode_fwd reads them); rows whose
+ *     position would be negative (L_b < s_new) are skipped.
+ * One kernel on `stream`. Contract the host cannot check: block_table[b][j]
+ * is a valid block for every block the new positions fall in, and no two
+ * new rows map to the same cache row.
+ * Errors: MLA_ERR_INVALID_ARG (null or misaligned pointer, non-positive
+ *   size), MLA_ERR_UNSUPPORTED (more than 2^33 rows), MLA_ERR_HIP.
+ */
+int mla_append_kv(void* kcache, int64_t nblocks, const int32_t* block_table, int max_blocks,
+                  const int32_t* cache_seqlens, const void* new_rows, int batch, int s_new, void* stream);
+
+/*
+ * Paged block pool: host-side bookkeeping of which physical cache blocks
+ * belong to which sequence, so that a sequence's blocks need not be
+ * contiguous and freed blocks are reused (FlashMLA explainer, section 4.3.2
+ * "Paged KV Cache": fixed-size pages allocated on demand, like virtual
+ * memory). The pool allocates host memory only and makes no HIP call; the
+ * caller copies the tables it produces to the device. A pool is not
+ * thread-safe: calls on one pool must not overlap.
+ *
+ * mla_block_pool_create: a pool of physical blocks [0, nblocks) for
+ *   sequence slots [0, max_seqs), each of at most max_blocks_per_seq blocks.
+ *   Blocks are handed out lowest id first; freed blocks are reused last
+ *   freed first. *pool receives the handle (NULL on error).
+ * mla_block_pool_reserve: make slot `seq` hold ceil(new_len / 64) blocks and
+ *   set its length to new_len: blocks are appended when it grows and the
+ *   tail blocks freed when it shrinks; kept blocks keep their ids, so rows
+ *   already cached stay where they are. MLA_ERR_OUT_OF_BLOCKS if the free
+ *   blocks do not suffice (the pool is left unchanged).
+ * mla_block_pool_release: reserve(seq, 0): frees all blocks of the slot.
+ * mla_block_pool_free_blocks: number of free blocks (-1 for NULL).
+ * mla_block_pool_table: for slots seqs[0..n), writes row k of table (host
+ *   int32 [n, max_blocks]) = the slot's block ids, padded with -1, and
+ *   lens[k] = its length (lens may be NULL); MLA_ERR_INVALID_ARG if a slot
+ *   holds more than max_blocks blocks.
+ * Errors: MLA_ERR_INVALID_ARG (NULL pool, slot out of range, negative
+ *   length, more than max_blocks_per_seq blocks), MLA_ERR_OUT_OF_MEMORY.
+ */
+int mla_block_pool_create(int64_t nblocks, int max_seqs, int max_blocks_per_seq, void** pool);
+void mla_block_pool_destroy(void* pool);
+int mla_block_pool_reserve(void* pool, int seq, int new_len);
+int mla_block_pool_release(void* pool, int seq);
+int64_t mla_block_pool_free_blocks(const void* pool);
+int mla_block_pool_table(const void* pool, const int32_t* seqs, int n, int max_blocks, int32_t* table,
+                         int32_t* lens);
 
 #ifdef __cplusplus
 }

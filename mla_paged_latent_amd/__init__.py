@@ -60,6 +60,20 @@ def load_library(path: Path | str | None = None):
         getattr(lib, name).argtypes = dec
     lib.mla_combine_splits.restype = i32
     lib.mla_combine_splits.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.mla_append_kv.restype = i32
+    lib.mla_append_kv.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, vp]
+    lib.mla_block_pool_create.restype = i32
+    lib.mla_block_pool_create.argtypes = [i64, i32, i32, ctypes.POINTER(vp)]
+    lib.mla_block_pool_destroy.restype = None
+    lib.mla_block_pool_destroy.argtypes = [vp]
+    lib.mla_block_pool_reserve.restype = i32
+    lib.mla_block_pool_reserve.argtypes = [vp, i32, i32]
+    lib.mla_block_pool_release.restype = i32
+    lib.mla_block_pool_release.argtypes = [vp, i32]
+    lib.mla_block_pool_free_blocks.restype = i64
+    lib.mla_block_pool_free_blocks.argtypes = [vp]
+    lib.mla_block_pool_table.restype = i32
+    lib.mla_block_pool_table.argtypes = [vp, vp, i32, i32, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -226,6 +240,75 @@ def mla_combine_splits(num_splits, s_q: int, h_q: int, num_units: int, out, lse,
     return out, lse
 
 
+def mla_append_kv(kcache, block_table, cache_seqlens, new_rows):
+    """Cache append: new_rows bf16 [B, s_new, 576] go to token positions
+    cache_seqlens[b] - s_new + i of their sequence (cache_seqlens counts them).
+    kcache bf16 [nblocks, 64, 576] is updated in place and returned."""
+    import torch
+    _need(kcache, torch.bfloat16, "kcache")
+    dev = kcache.device
+    _need(block_table, torch.int32, "block_table", dev)
+    _need(cache_seqlens, torch.int32, "cache_seqlens", dev)
+    _need(new_rows, torch.bfloat16, "new_rows", dev)
+    if kcache.dim() != 3 or kcache.shape[1] != PAGE_SIZE or kcache.shape[2] != D_QK:
+        raise ValueError("kcache must be [nblocks, 64, 576]")
+    if new_rows.dim() != 3 or new_rows.shape[2] != D_QK:
+        raise ValueError("new_rows must be [B, s_new, 576]")
+    B, s_new = int(new_rows.shape[0]), int(new_rows.shape[1])
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and cache_seqlens [B]")
+    with _on(torch, dev):
+        _check("mla_append_kv", load_library().mla_append_kv(
+            kcache.data_ptr(), int(kcache.shape[0]), block_table.data_ptr(), int(block_table.shape[1]),
+            cache_seqlens.data_ptr(), new_rows.data_ptr(), B, s_new, _stream(torch)))
+    return kcache
+
+
+class BlockPool:
+    """Host bookkeeping of the paged cache's blocks (mla_block_pool_* in the
+    library): per-slot block lists that grow and shrink, and the block tables
+    the device calls take."""
+
+    def __init__(self, nblocks: int, max_seqs: int, max_blocks_per_seq: int):
+        self._lib = load_library()
+        h = ctypes.c_void_p(None)
+        _check("mla_block_pool_create", self._lib.mla_block_pool_create(int(nblocks), int(max_seqs),
+                                                                        int(max_blocks_per_seq), ctypes.byref(h)))
+        self._h = h
+        self.nblocks, self.max_seqs, self.max_blocks_per_seq = int(nblocks), int(max_seqs), int(max_blocks_per_seq)
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            self._lib.mla_block_pool_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reserve(self, seq: int, new_len: int):
+        """Give slot seq room for new_len tokens (and make that its length)."""
+        _check("mla_block_pool_reserve", self._lib.mla_block_pool_reserve(self._h, int(seq), int(new_len)))
+
+    def release(self, seq: int):
+        _check("mla_block_pool_release", self._lib.mla_block_pool_release(self._h, int(seq)))
+
+    def free_blocks(self) -> int:
+        return int(self._lib.mla_block_pool_free_blocks(self._h))
+
+    def table(self, seqs, max_blocks: int):
+        """(block_table int32 [n, max_blocks] padded with -1, lengths int32 [n]) as numpy arrays."""
+        seqs = np.ascontiguousarray(np.asarray(seqs), dtype=np.int32)
+        n = int(seqs.shape[0])
+        table = np.zeros((n, int(max_blocks)), dtype=np.int32)
+        lens = np.zeros((n,), dtype=np.int32)
+        _check("mla_block_pool_table", self._lib.mla_block_pool_table(self._h, seqs.ctypes.data, n, int(max_blocks),
+                                                                      table.ctypes.data, lens.ctypes.data))
+        return table, lens
+
+
 def workspace_bytes(batch: int, s_q: int, h_q: int, num_units: int) -> int:
     """Workspace mla_decode_fwd needs for a plan of num_units units (asks the library)."""
     n = ctypes.c_size_t(0)
@@ -234,6 +317,6 @@ def workspace_bytes(batch: int, s_q: int, h_q: int, num_units: int) -> int:
 
 
 __all__ = ["mla_plan_sizes", "mla_workspace_bytes", "mla_get_metadata", "mla_get_metadata_host", "mla_decode_fwd",
-           "mla_decode_fwd_splits", "mla_combine_splits",
+           "mla_decode_fwd_splits", "mla_combine_splits", "mla_append_kv", "BlockPool",
            "workspace_bytes", "load_library", "status_string", "MLAError", "LIB_PATH",
            "D_QK", "D_V", "PAGE_SIZE", "META_INTS"]

@@ -75,6 +75,8 @@ const char* mla_status_string(int status)
     case MLA_ERR_UNSUPPORTED: return "unsupported shape (s_q*h_q must be a multiple of 16 in [16, 1024], batch <= 16384)";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mla_plan_sizes reports";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_OUT_OF_BLOCKS: return "block pool has too few free blocks";
+    case MLA_ERR_OUT_OF_MEMORY: return "host allocation failed";
     default: return "unknown status";
     }
 }

@@ -186,3 +186,44 @@ def algorithmic_counts(seqlens, s_q: int, h_q: int, causal: bool,
     vis = visible_tokens(L, s_q, causal)
     flops = int(vis.sum()) * h_q * 2 * (d_qk + d_v)
     return nbytes, flops
+
+
+# ---------------------------------------------------------------- cache append
+
+APPEND_SEED = 11
+APPEND_DESCRIPTION = "B=64 sequences, 512 new tokens each, cache_seqlens U[1024,4096] after the append"
+
+
+@dataclass
+class AppendInputs:
+    """One cache-append batch (host numpy; bf16 as uint16 bits)."""
+    kcache: np.ndarray          # uint16 [nblocks, 64, 576]
+    block_table: np.ndarray     # int32  [B, max_blocks]
+    cache_seqlens: np.ndarray   # int32  [B], lengths including the new tokens
+    new_rows: np.ndarray        # uint16 [B, s_new, 576]
+
+
+def make_append(batch: int = 64, s_new: int = 512, seed: int = APPEND_SEED) -> AppendInputs:
+    """Lengths U[1024, 4096] after the append, a shuffled block table as for the
+    decode workloads, an N(0,1) cache and N(0,1) new rows, seeded."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1024, 4097, batch).astype(np.int32)
+    nb = (lens + PAGE - 1) // PAGE
+    nblocks = int(nb.sum()) + 4
+    perm = rng.permutation(nblocks).astype(np.int32)
+    table = np.full((batch, int(nb.max())), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(nb):
+        table[b, :n] = perm[off:off + n]
+        off += int(n)
+    kcache = f32_to_bf16_bits(rng.standard_normal((nblocks, PAGE, D_QK), dtype=np.float32))
+    new_rows = f32_to_bf16_bits(rng.standard_normal((batch, s_new, D_QK), dtype=np.float32))
+    return AppendInputs(kcache=kcache, block_table=table, cache_seqlens=lens, new_rows=new_rows)
+
+
+def append_bytes(inp: AppendInputs) -> int:
+    """Algorithmic HBM bytes of one append: every new row read once and written
+    once, plus the block-table entries and lengths the kernel reads."""
+    B, s_new, width = inp.new_rows.shape
+    rows = int(np.minimum(inp.cache_seqlens, s_new).sum())
+    return 2 * rows * width * 2 + 4 * rows + 4 * B
