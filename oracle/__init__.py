@@ -15,18 +15,22 @@ import numpy as np
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "mla_oracle.c"
+_SRC_SPARSE = _HERE / "mla_oracle_sparse.c"
 _BUILD = _HERE / "_build"
 _LIB = _BUILD / "liboracle.so"
 _lib = None
 
 
-def build(force: bool = False, src: Path = _SRC, out: Path = _LIB) -> Path:
-    """Compile the oracle with gcc (no GPU code, no HIP headers)."""
+def build(force: bool = False, src=None, out: Path = _LIB) -> Path:
+    """Compile the oracle with gcc (no GPU code, no HIP headers). src: one C
+    file or a list of them (default: the dense and the sparse decode oracle)."""
+    srcs = [_SRC, _SRC_SPARSE] if src is None else ([src] if isinstance(src, (str, Path)) else list(src))
+    srcs = [Path(x) for x in srcs]
     out.parent.mkdir(parents=True, exist_ok=True)
-    if force or not out.exists() or out.stat().st_mtime < src.stat().st_mtime:
+    if force or not out.exists() or any(out.stat().st_mtime < x.stat().st_mtime for x in srcs):
         tmp = out.with_suffix(".so.tmp%d" % os.getpid())
         subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-                        str(src), "-o", str(tmp), "-lm"], check=True)
+                        *[str(x) for x in srcs], "-o", str(tmp), "-lm"], check=True)
         os.replace(tmp, out)
     return out
 
@@ -47,6 +51,11 @@ def load(path: Path | None = None):
                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    if hasattr(lib, "mla_oracle_decode_sparse"):
+        sp = lib.mla_oracle_decode_sparse
+        sp.restype = ctypes.c_int
+        sp.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_void_p,
+                                                                     ctypes.c_void_p, ctypes.c_int]
     if path is None:
         _lib = lib
     return lib
@@ -95,3 +104,34 @@ def decode_inputs(inp, nthreads: int | None = None, lib=None):
     """Oracle decode of a workloads.DecodeInputs."""
     return mla_decode(inp.q, inp.kcache, inp.block_table, inp.cache_seqlens,
                       inp.softmax_scale, inp.causal, nthreads=nthreads, lib=lib)
+
+
+def mla_decode_sparse(q, kcache, block_table, indices, counts, softmax_scale, nthreads: int | None = None,
+                      d_v: int = 512, lib=None):
+    """Oracle sparse decode: query row (b, i, h) attends over the tokens
+    indices[b, i, :counts[b*s_q+i]] (entries < 0 skipped).
+
+    q uint16 [B, s_q, h_q, d_qk]; kcache uint16 [nblocks, page, d_qk];
+    block_table int32 [B, max_blocks]; indices int32 [B, s_q, topk];
+    counts int32 [B * s_q]. Returns (out float64 [B, s_q, h_q, d_v], lse float64 [B, s_q, h_q]).
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kcache = np.ascontiguousarray(kcache, dtype=np.uint16)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    indices = np.ascontiguousarray(indices, dtype=np.int32)
+    counts = np.ascontiguousarray(np.asarray(counts).reshape(-1), dtype=np.int32)
+    B, s_q, h_q, d_qk = q.shape
+    nblocks, page, _ = kcache.shape
+    if indices.ndim != 3 or indices.shape[:2] != (B, s_q) or counts.shape != (B * s_q,):
+        raise ValueError("indices must be [B, s_q, topk] and counts [B * s_q]")
+    topk = indices.shape[2]
+    out = np.zeros((B, s_q, h_q, d_v), dtype=np.float64)
+    lse = np.zeros((B, s_q, h_q), dtype=np.float64)
+    lib = lib or load()
+    rc = lib.mla_oracle_decode_sparse(q.ctypes.data, kcache.ctypes.data, block_table.ctypes.data,
+                                      indices.ctypes.data, counts.ctypes.data, B, s_q, h_q,
+                                      block_table.shape[1], topk, d_qk, d_v, page, float(softmax_scale),
+                                      out.ctypes.data, lse.ctypes.data, int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("sparse oracle failed (%d)" % rc)
+    return out, lse
