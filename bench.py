@@ -209,6 +209,91 @@ def bench_append(args, torch, mla, dev):
     return 0
 
 
+def bench_sparse(args, torch, mla, dev):
+    """Sparse decode: plan (mla_get_metadata_sparse) + mla_decode_sparse_fwd per step."""
+    sp = wl.make_sparse()
+    d = sp.dec
+    B, s_q, h_q = d.batch, d.s_q, d.h_q
+    topk = sp.indices.shape[2]
+    nbytes, flops = wl.sparse_counts(sp)
+    rep_bytes = d.kcache.nbytes + d.q.nbytes
+    R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / rep_bytes))
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    table = torch.from_numpy(d.block_table).to(dev)
+    idx = torch.from_numpy(sp.indices).to(dev)
+    lens = torch.from_numpy(sp.counts).to(dev)
+    reps = [(bf16(d.kcache), bf16(d.q)) for _ in range(R)]
+    sizes = mla.mla_sparse_plan_sizes(B, s_q, h_q, topk)
+    units = sizes["num_units"]
+    meta = torch.empty((units, mla.META_INTS), dtype=torch.int32, device=dev)
+    splits = torch.empty((B * s_q + 1,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, s_q, h_q, mla.D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+    ws = torch.empty((sizes["workspace_bytes"],), dtype=torch.uint8, device=dev)
+
+    def step(k):
+        kc, q = reps[k % R]
+        mla.mla_get_metadata_sparse(lens, B, s_q, h_q, topk, num_units=units, tile_meta=meta, num_splits=splits)
+        mla.mla_decode_sparse_fwd(q, kc, table, idx, lens, d.softmax_scale, meta, splits, out=out, lse=lse,
+                                  workspace=ws)
+
+    for k in range(max(args.warmup, R)):
+        step(k)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for k in range(args.steps):
+            step(k)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "MLA sparse (top-k) decode HBM GB/s + TFLOPS (fraction of MI355X peak), paged bf16",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "sparse: " + wl.SPARSE_DESCRIPTION + ", d_qk=576, d_v=512, block 64, shuffled "
+                               "block_table, bf16 N(0,1), scale 1/sqrt(192)",
+                   "batch": B, "s_q": s_q, "h_q": h_q, "topk": topk, "replicas": R, "num_units": units},
+        "tflops": round(tf, 3), "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
+        "roofline": {"bound": "hbm", "kernel": "sparse decode step (plan + decode + combine)", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_ms_avg": round(ms, 6)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        nth = orc.default_threads()
+        sample = [0, 1, 2, 3]
+        sub = wl.subset(d, sample)
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            orc.mla_decode_sparse(sub.q, sub.kcache, sub.block_table, sp.indices[sample], sp.counts[sample],
+                                  d.softmax_scale, nthreads=nth)
+            n += 1
+            if time.perf_counter() - t0 >= min(args.cpu_seconds, 10.0) or n >= 20:
+                break
+        sec = (time.perf_counter() - t0) / n * (B / len(sample))
+        result["cpu_baseline"] = {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": nth,
+                                  "kind": "oracle",
+                                  "sample": "%d passes over sequences %s of the batch, scaled to all %d" % (n, sample, B)}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,8 +309,9 @@ def main(argv=None):
                     help="no GPU: write the workload's HBM bytes per decode launch to profiles/decode_traffic.json "
                          "from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv outputs")
     ap.add_argument("--copy-bytes", type=int, default=256 * 2 ** 20, help="size of the calibration copy")
-    ap.add_argument("--op", default="decode", choices=["decode", "append"],
-                    help="decode: the hot path (default); append: the cache-append kernel alone")
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "sparse"],
+                    help="decode: the hot path (default); append: the cache-append kernel alone; "
+                         "sparse: top-k index decode (plan + decode + combine)")
     args = ap.parse_args(argv)
     if args.pmc_summary:
         return pmc_summary(args)
@@ -256,6 +342,8 @@ def main(argv=None):
     mla.load_library()
     if args.op == "append":
         return bench_append(args, torch, mla, dev)
+    if args.op == "sparse":
+        return bench_sparse(args, torch, mla, dev)
     inp = wl.make_workload(args.workload, poison=False)
     B, s_q, h_q = inp.batch, inp.s_q, inp.h_q
     nbytes, flops = wl.algorithmic_counts(inp.cache_seqlens, s_q, h_q, inp.causal)

@@ -179,6 +179,45 @@ int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, i
                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Sparse (top-k index) decode: each new token attends over its own list of
+ * cached token positions instead of all of them -- the dynamic sparse
+ * attention of DeepSeek v3.2 named on the "Boosting DeepSeek V3.2" page
+ * (leadinhealth.com), an indexer choosing the tokens each query attends to.
+ * The attention itself is that of mla_decode_fwd restricted to the listed
+ * rows; all heads of a new token share its list. Readings where the pages are
+ * silent: list entries < 0 are padding and skipped; a repeated position
+ * counts once per occurrence; no causal mask beyond the list; a list with no
+ * valid entry gives out = 0, lse = -inf.
+ *
+ * mla_sparse_plan_sizes: like mla_plan_sizes for a sparse batch (topk = the
+ *   list capacity, 1..2048; h_q a multiple of 16 in [16, 1024]; batch*s_q
+ *   lists at most 16384).
+ * mla_get_metadata_sparse: the split plan of the batch*s_q lists (one small
+ *   kernel on `stream`), from topk_lens: device int32 [batch*s_q], the number
+ *   of leading list entries in use, 0..topk. tile_meta / num_splits as for
+ *   mla_get_metadata with batch*s_q "sequences".
+ * mla_decode_sparse_fwd: the decode. q, kcache, block_table, out, lse,
+ *   workspace as for mla_decode_fwd; indices: device int32 [batch, s_q, topk],
+ *   list of new token i of sequence b = indices[b][i][0 .. topk_lens[b*s_q+i]).
+ *   Contracts the host cannot check: 0 <= topk_lens[.] <= topk; a listed
+ *   position t has a valid block block_table[b][t / 64] (entries with t / 64
+ *   >= max_blocks or a negative table entry are treated as padding).
+ * Errors: as for mla_plan_sizes / mla_get_metadata / mla_decode_fwd
+ *   (MLA_ERR_UNSUPPORTED for topk > 2048, h_q not a multiple of 16).
+ */
+int mla_sparse_plan_sizes(int batch, int s_q, int h_q, int topk, int num_cus, int* num_units,
+                          size_t* meta_bytes, size_t* splits_bytes, size_t* workspace_bytes);
+int mla_get_metadata_sparse(const int32_t* topk_lens, int batch, int s_q, int h_q, int topk, int num_units,
+                            int32_t* tile_meta, int32_t* num_splits, void* stream);
+int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks,
+                          const int32_t* block_table, int max_blocks,
+                          const int32_t* indices, const int32_t* topk_lens, int topk,
+                          int batch, int s_q, int h_q, float softmax_scale,
+                          const int32_t* tile_meta, const int32_t* num_splits, int num_units,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * Cache append: writes the new tokens' cached rows into their blocks, the
  * step that precedes decode attention over them (the cache grows by the new
  * tokens' entries each step: "OpenSourceWeek Day 1: FlashMLA", "How KV

@@ -60,6 +60,14 @@ def load_library(path: Path | str | None = None):
         getattr(lib, name).argtypes = dec
     lib.mla_combine_splits.restype = i32
     lib.mla_combine_splits.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.mla_sparse_plan_sizes.restype = i32
+    lib.mla_sparse_plan_sizes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(sz),
+                                          ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.mla_get_metadata_sparse.restype = i32
+    lib.mla_get_metadata_sparse.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_decode_sparse_fwd.restype = i32
+    lib.mla_decode_sparse_fwd.argtypes = [vp, vp, i64, vp, i32, vp, vp, i32, i32, i32, i32, ctypes.c_float,
+                                          vp, vp, i32, vp, vp, vp, sz, vp]
     lib.mla_append_kv.restype = i32
     lib.mla_append_kv.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, vp]
     lib.mla_block_pool_create.restype = i32
@@ -240,6 +248,83 @@ def mla_combine_splits(num_splits, s_q: int, h_q: int, num_units: int, out, lse,
     return out, lse
 
 
+def mla_sparse_plan_sizes(batch: int, s_q: int, h_q: int, topk: int, num_cus: int = 0) -> dict:
+    """Plan geometry and buffer sizes of a sparse decode batch (host only)."""
+    units = ctypes.c_int(0)
+    meta, splits, ws = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mla_sparse_plan_sizes", load_library().mla_sparse_plan_sizes(
+        batch, s_q, h_q, topk, num_cus, ctypes.byref(units), ctypes.byref(meta), ctypes.byref(splits),
+        ctypes.byref(ws)))
+    return {"num_units": units.value, "meta_bytes": meta.value, "splits_bytes": splits.value,
+            "workspace_bytes": ws.value}
+
+
+def mla_get_metadata_sparse(topk_lens, batch: int, s_q: int, h_q: int, topk: int, num_units: int | None = None,
+                            tile_meta=None, num_splits=None):
+    """Split plan of a sparse batch on the device from topk_lens int32 [batch * s_q].
+    Returns (tile_meta int32 [G, 8], num_splits int32 [batch * s_q + 1])."""
+    import torch
+    _need(topk_lens, torch.int32, "topk_lens")
+    dev = topk_lens.device
+    if tuple(topk_lens.shape) != (batch * s_q,):
+        raise ValueError("topk_lens must be [batch * s_q]")
+    with _on(torch, dev):
+        if num_units is None:
+            num_units = mla_sparse_plan_sizes(batch, s_q, h_q, topk)["num_units"]
+        if tile_meta is None:
+            tile_meta = torch.empty((num_units, META_INTS), dtype=torch.int32, device=dev)
+        if num_splits is None:
+            num_splits = torch.empty((batch * s_q + 1,), dtype=torch.int32, device=dev)
+        _check("mla_get_metadata_sparse", load_library().mla_get_metadata_sparse(
+            topk_lens.data_ptr(), batch, s_q, h_q, topk, num_units, tile_meta.data_ptr(), num_splits.data_ptr(),
+            _stream(torch)))
+    return tile_meta, num_splits
+
+
+def mla_decode_sparse_fwd(q, kcache, block_table, indices, topk_lens, softmax_scale: float, tile_meta, num_splits,
+                          out=None, lse=None, workspace=None):
+    """Sparse decode: q bf16 [B, s_q, h_q, 576] attends, per new token, over the
+    cached positions indices[b, i, :topk_lens[b*s_q+i]] (int32 [B, s_q, topk];
+    entries < 0 are padding). Returns (out bf16 [B, s_q, h_q, 512], lse f32 [B, s_q, h_q])."""
+    import torch
+    _need(q, torch.bfloat16, "q")
+    dev = q.device
+    _need(kcache, torch.bfloat16, "kcache", dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    _need(indices, torch.int32, "indices", dev)
+    _need(topk_lens, torch.int32, "topk_lens", dev)
+    _need(tile_meta, torch.int32, "tile_meta", dev)
+    _need(num_splits, torch.int32, "num_splits", dev)
+    if q.dim() != 4 or q.shape[3] != D_QK:
+        raise ValueError("q must be [B, s_q, h_q, 576]")
+    if kcache.dim() != 3 or kcache.shape[1] != PAGE_SIZE or kcache.shape[2] != D_QK:
+        raise ValueError("kcache must be [nblocks, 64, 576]")
+    B, s_q, h_q, _ = q.shape
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (B, s_q) or tuple(topk_lens.shape) != (B * s_q,):
+        raise ValueError("indices must be [B, s_q, topk] and topk_lens [B * s_q]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    topk = int(indices.shape[2])
+    num_units = int(tile_meta.shape[0])
+    with _on(torch, dev):
+        if out is None:
+            out = torch.empty((B, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+        if workspace is None:
+            ws = mla_sparse_plan_sizes(B, s_q, h_q, topk)["workspace_bytes"]
+            n = ctypes.c_size_t(0)
+            _check("mla_workspace_bytes", load_library().mla_workspace_bytes(B * s_q, 1, h_q, num_units,
+                                                                              ctypes.byref(n)))
+            workspace = torch.empty((max(ws, n.value, 16),), dtype=torch.uint8, device=dev)
+        _check("mla_decode_sparse_fwd", load_library().mla_decode_sparse_fwd(
+            q.data_ptr(), kcache.data_ptr(), int(kcache.shape[0]), block_table.data_ptr(), int(block_table.shape[1]),
+            indices.data_ptr(), topk_lens.data_ptr(), topk, B, s_q, h_q, float(softmax_scale), tile_meta.data_ptr(),
+            num_splits.data_ptr(), num_units, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+            int(workspace.numel()), _stream(torch)))
+    return out, lse
+
+
 def mla_append_kv(kcache, block_table, cache_seqlens, new_rows):
     """Cache append: new_rows bf16 [B, s_new, 576] go to token positions
     cache_seqlens[b] - s_new + i of their sequence (cache_seqlens counts them).
@@ -318,5 +403,6 @@ def workspace_bytes(batch: int, s_q: int, h_q: int, num_units: int) -> int:
 
 __all__ = ["mla_plan_sizes", "mla_workspace_bytes", "mla_get_metadata", "mla_get_metadata_host", "mla_decode_fwd",
            "mla_decode_fwd_splits", "mla_combine_splits", "mla_append_kv", "BlockPool",
+           "mla_sparse_plan_sizes", "mla_get_metadata_sparse", "mla_decode_sparse_fwd",
            "workspace_bytes", "load_library", "status_string", "MLAError", "LIB_PATH",
            "D_QK", "D_V", "PAGE_SIZE", "META_INTS"]

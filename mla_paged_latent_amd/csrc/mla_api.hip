@@ -12,6 +12,7 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_u
                        int32_t* splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_decode_sparse(const DecodeParams& p, int num_units, int head_groups, hipStream_t stream);
 }  // namespace mla
 
 namespace {
@@ -185,6 +186,9 @@ int setup_decode(const void* q, const void* kcache, int64_t nblocks, const int32
     p->rows_total = geo.rows_total;
     p->causal = causal ? 1 : 0;
     p->scale_log2 = softmax_scale * 1.4426950408889634f;
+    p->indices = nullptr;
+    p->topk = 0;
+    p->sq_real = 1;
     *geo_out = geo;
     return MLA_OK;
 }
@@ -261,6 +265,115 @@ int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, i
     p.batch = batch;
     p.rows_total = geo.rows_total;
     return run_combine(p, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- sparse decode
+//
+// A sparse batch of `batch` sequences with s_q new tokens each is planned and
+// decoded as a batch of batch*s_q token lists of h_q rows each (the streaming
+// kernel with its per-list plan); the lists' lengths play the part of
+// cache_seqlens.
+
+namespace {
+
+constexpr int kMaxTopk = 2048;
+
+int check_sparse_shape(int batch, int s_q, int h_q, int topk)
+{
+    if (batch < 1 || s_q < 1 || h_q < 1 || topk < 1) return MLA_ERR_INVALID_ARG;
+    if ((long)batch * s_q > kMaxBatch || h_q % 16 != 0 || h_q > mla::kMaxRows || topk > kMaxTopk)
+        return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_sparse_plan_sizes(int batch, int s_q, int h_q, int topk, int num_cus, int* num_units, size_t* meta_bytes,
+                          size_t* splits_bytes, size_t* workspace_bytes)
+{
+    int rc = check_sparse_shape(batch, s_q, h_q, topk);
+    if (rc != MLA_OK) return rc;
+    if (num_cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+        if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return MLA_ERR_HIP;
+        if (num_cus <= 0) return MLA_ERR_HIP;
+    }
+    const int lists = batch * s_q;
+    int units = num_cus / (h_q / 16);
+    if (units < lists + 1) units = lists + 1;
+    size_t part_o = 0, total = 0;
+    workspace_layout(lists, h_q, units, &part_o, &total);
+    if (num_units) *num_units = units;
+    if (meta_bytes) *meta_bytes = (size_t)units * mla::kMetaInts * sizeof(int32_t);
+    if (splits_bytes) *splits_bytes = (size_t)(lists + 1) * sizeof(int32_t);
+    if (workspace_bytes) *workspace_bytes = total;
+    return MLA_OK;
+}
+
+int mla_get_metadata_sparse(const int32_t* topk_lens, int batch, int s_q, int h_q, int topk, int num_units,
+                            int32_t* tile_meta, int32_t* num_splits, void* stream)
+{
+    int rc = check_sparse_shape(batch, s_q, h_q, topk);
+    if (rc != MLA_OK) return rc;
+    if (!topk_lens || !tile_meta || !num_splits) return MLA_ERR_INVALID_ARG;
+    if (num_units < batch * s_q + 1) return MLA_ERR_INVALID_ARG;
+    if (mla::launch_plan(topk_lens, batch * s_q, 16, num_units, tile_meta, num_splits, (hipStream_t)stream) !=
+        hipSuccess)
+        return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table,
+                          int max_blocks, const int32_t* indices, const int32_t* topk_lens, int topk, int batch,
+                          int s_q, int h_q, float softmax_scale, const int32_t* tile_meta,
+                          const int32_t* num_splits, int num_units, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    int rc = check_sparse_shape(batch, s_q, h_q, topk);
+    if (rc != MLA_OK) return rc;
+    if (!q || !kcache || !block_table || !indices || !topk_lens || !tile_meta || !num_splits || !out || !lse ||
+        !workspace)
+        return MLA_ERR_INVALID_ARG;
+    if (nblocks < 1 || nblocks > 0x7fffffff / mla::kPage || max_blocks < 1 || !isfinite(softmax_scale))
+        return MLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(out) || !aligned16(workspace) || ((uintptr_t)lse & 3u))
+        return MLA_ERR_INVALID_ARG;
+    const int lists = batch * s_q;
+    if (num_units < lists + 1) return MLA_ERR_INVALID_ARG;
+    size_t part_o = 0, total = 0;
+    workspace_layout(lists, h_q, num_units, &part_o, &total);
+    if (workspace_bytes < total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    mla::DecodeParams p;
+    p.q = (const uint16_t*)q;
+    p.kcache = (const uint16_t*)kcache;
+    p.block_table = block_table;
+    p.seqlens = topk_lens;
+    p.meta = tile_meta;
+    p.splits = num_splits;
+    p.out = (uint16_t*)out;
+    p.lse = lse;
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)((char*)workspace + part_o);
+    p.nblocks = nblocks;
+    p.max_blocks = max_blocks;
+    p.batch = lists;
+    p.s_q = 1;
+    p.h_q = h_q;
+    p.rows_total = h_q;
+    p.causal = 0;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.indices = indices;
+    p.topk = topk;
+    p.sq_real = s_q;
+    hipStream_t st = (hipStream_t)stream;
+    if (mla::launch_decode_sparse(p, num_units, h_q / 16, st) != hipSuccess) return MLA_ERR_HIP;
+    return run_combine(p, st);
 }
 
 }  // extern "C"

@@ -110,6 +110,11 @@ struct DecodeParams {
     int rows_total;
     int causal;
     float scale_log2;           // softmax_scale * log2(e)
+    // sparse decode only: "sequence" b is new token b % sq_real of sequence
+    // b / sq_real, and its token t is cached position indices[b * topk + t]
+    const int32_t* indices;
+    int topk;
+    int sq_real;
 };
 
 struct CombineParams {

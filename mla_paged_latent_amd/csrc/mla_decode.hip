@@ -73,12 +73,19 @@ __device__ __forceinline__ void copy_rows(const unsigned char* gbase, int valid,
 constexpr int kSlotA = 19 * 1024;        // 16 rows x 1168 B, rounded up to whole 1 KB copies
 constexpr int kDmaA = 19;
 constexpr int kLdsA = 8 * kSlotA;        // two slots per wave: 155,648 B
+constexpr int kMaxTopk = 2048;           // sparse decode: longest token list
+constexpr int kRowTabB = kMaxTopk * 4;   // sparse decode: cache row of each listed token of the unit
 
-template <int NR>
+// SPARSE: the unit's tokens are entries of a token list rather than a run of
+// cache blocks (sparse decode). Before any copy the workgroup translates its
+// list entries into cache row numbers (block_table[page] * 64 + row) in LDS,
+// -1 for padding; a sub-tile's 16 rows are then copied from 16 unrelated
+// places, padding rows from the unit's first listed row (finite data, masked).
+template <int NR, bool SPARSE>
 __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
 {
     constexpr int R = 16 * NR;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsA];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsA + (SPARSE ? kRowTabB : 0)];
     const unsigned lds0 = lds_base(smem);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -94,12 +101,38 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     const int nsplit = meta[7];
     if (b >= p.batch || j0 >= j1) return;
     const int tok_begin = j0 * kPage;
-    const int tok_end = min(j1 * kPage, L);
-    const int nsub = (tok_end - tok_begin + 15) >> 4;
-    const int K = nsub > wave ? (nsub - wave + 3) >> 2 : 0;   // this wave's sub-tiles: wave, wave+4, ...
+    const int tok_end = SPARSE ? min(min(j1 * kPage, L), p.topk) : min(j1 * kPage, L);
+    const int nsub = tok_end > tok_begin ? (tok_end - tok_begin + 15) >> 4 : 0;
+    int K = nsub > wave ? (nsub - wave + 3) >> 2 : 0;         // this wave's sub-tiles: wave, wave+4, ...
     const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
     const int npages = j1 - j0;
-    const int page_vec = lane < npages ? table[j0 + lane] : 0;
+    const int page_vec = (!SPARSE && lane < npages) ? table[j0 + lane] : 0;
+    const unsigned rowtab = lds0 + kLdsA;                   // SPARSE: int32 per listed token of the unit
+    int fallback = 0;                                       // SPARSE: cache row for padding entries
+    if constexpr (SPARSE) {
+        const int32_t* list = p.indices + (size_t)b * p.topk;
+        const int32_t* rtable = p.block_table + (size_t)(b / p.sq_real) * p.max_blocks;
+        for (int e = (int)threadIdx.x; e < tok_end - tok_begin; e += 256) {
+            const int t = list[tok_begin + e];
+            int rowid = -1;
+            if (t >= 0 && (t >> 6) < p.max_blocks) {
+                const int pg = rtable[t >> 6];
+                if (pg >= 0 && (int64_t)pg < p.nblocks) rowid = pg * kPage + (t & (kPage - 1));
+            }
+            *(__attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)e) = rowid;
+        }
+        settle_loads();
+        wg_barrier();
+        fallback = -1;
+        for (int c0 = 0; c0 < tok_end - tok_begin && fallback < 0; c0 += 64) {
+            const int v = c0 + lane < tok_end - tok_begin
+                              ? *(const __attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)(c0 + lane))
+                              : -1;
+            const unsigned long long any = __builtin_amdgcn_ballot_w64(v >= 0);
+            if (any) fallback = __builtin_amdgcn_readlane(v, __builtin_ctzll(any));
+        }
+        if (fallback < 0) K = 0;                            // no listed token: an empty partial
+    }
 
     float mrun[NR], lrun[NR];
     f32x4 acc[NR][32];
@@ -114,6 +147,21 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     const unsigned slot0 = lds0 + (unsigned)(2 * wave) * kSlotA;
     auto issue = [&](int k) {
         const int tok = tok_begin + 16 * (wave + 4 * k);
+        if constexpr (SPARSE) {
+            const unsigned dst = slot0 + (unsigned)(k & 1) * kSlotA;
+            for (int i = 0; i < kDmaA; ++i) {
+                const int q = i * 64 + lane;
+                const int r = q / kRowSlots;
+                int c = q - r * kRowSlots;
+                c = c < kChunks ? c : 0;
+                int rowid = tok + r < tok_end
+                                ? *(const __attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)(tok - tok_begin + r))
+                                : -1;
+                rowid = rowid >= 0 ? rowid : fallback;
+                dma16((const unsigned char*)p.kcache + (size_t)rowid * kRowBytes + c * 16, dst + (unsigned)i * 1024u);
+            }
+            return;
+        }
         const int pidx = (tok >> 6) - j0;
         const int page = pidx < 64 ? __builtin_amdgcn_readlane(page_vec, pidx) : sload(table + j0 + pidx);
         const unsigned char* gbase = (const unsigned char*)p.kcache + (size_t)page * kPageBytes +
@@ -152,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     for (int rt = 0; rt < NR; ++rt) {
         const int row = blockIdx.y * R + rt * 16 + c16;
         const int iq = row / p.h_q;
-        lim[rt] = min(tok_end, p.causal ? L - (p.s_q - 1 - iq) : L);
+        lim[rt] = SPARSE ? tok_end : min(tok_end, p.causal ? L - (p.s_q - 1 - iq) : L);
     }
 
     const unsigned a_off = (unsigned)(token_of_row(c16) * kLdsRow + g * 16);
@@ -195,7 +243,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = tok0 + token_of_row(4 * g + i);
-                const float v = (t < lim[rt]) ? s[rt][i] * p.scale_log2 : -INFINITY;
+                bool vis = t < lim[rt];
+                if constexpr (SPARSE)
+                    vis = vis && *(const __attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)(t - tok_begin)) >= 0;
+                const float v = vis ? s[rt][i] * p.scale_log2 : -INFINITY;
                 s[rt][i] = v;
                 tmax = fmaxf(tmax, v);
             }
@@ -361,10 +412,17 @@ hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, 
 {
     dim3 grid(num_units, head_groups);
     switch (rows_wg) {
-    case 16: hipLaunchKernelGGL((decode_stream_kernel<1>), grid, dim3(256), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((decode_stream_kernel<1, false>), grid, dim3(256), 0, stream, p); break;
     case 64: return launch_wide(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_sparse(const DecodeParams& p, int num_units, int head_groups, hipStream_t stream)
+{
+    dim3 grid(num_units, head_groups);
+    hipLaunchKernelGGL((decode_stream_kernel<1, true>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -227,3 +227,45 @@ def append_bytes(inp: AppendInputs) -> int:
     B, s_new, width = inp.new_rows.shape
     rows = int(np.minimum(inp.cache_seqlens, s_new).sum())
     return 2 * rows * width * 2 + 4 * rows + 4 * B
+
+
+# ---------------------------------------------------------------- sparse decode
+
+SPARSE_SEED = 12
+SPARSE_DESCRIPTION = ("B=64, s_q=1, h_q=16, topk=2048 distinct positions drawn uniformly from [0, L), "
+                      "cache_seqlens U[4096,16384]")
+
+
+@dataclass
+class SparseInputs:
+    """One sparse-decode batch (host numpy; bf16 as uint16 bits)."""
+    dec: DecodeInputs           # q, kcache, block_table, cache_seqlens (non-causal)
+    indices: np.ndarray         # int32 [B, s_q, topk]
+    counts: np.ndarray          # int32 [B * s_q]
+
+
+def make_sparse(batch: int = 64, s_q: int = 1, h_q: int = 16, topk: int = 2048, lo: int = 4096, hi: int = 16384,
+                seed: int = SPARSE_SEED, poison: bool = False) -> SparseInputs:
+    """Lengths U[lo, hi], the decode recipe for the cache and queries, then for
+    every new token topk distinct positions of its sequence, uniformly drawn."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi + 1, batch).astype(np.int32)
+    dec = build_inputs(lens, s_q, h_q, rng, name="sparse", causal=False, poison=poison)
+    idx = np.empty((batch, s_q, topk), dtype=np.int32)
+    for b in range(batch):
+        for i in range(s_q):
+            idx[b, i] = rng.choice(int(lens[b]), size=topk, replace=False)
+    counts = np.full((batch * s_q,), topk, dtype=np.int32)
+    return SparseInputs(dec=dec, indices=idx, counts=counts)
+
+
+def sparse_counts(inp: SparseInputs):
+    """Algorithmic (bytes, flops) of one sparse decode: each listed row once per
+    new token (1152 B), q, out, lse and the list entries; 2*h*(576+512) flops
+    per listed row and head."""
+    d = inp.dec
+    B, s_q, h_q = d.batch, d.s_q, d.h_q
+    valid = int((inp.indices >= 0).sum())
+    nbytes = valid * D_QK * 2 + B * s_q * h_q * (D_QK * 2 + D_V * 2 + 4) + 4 * inp.indices.size + 4 * B * s_q
+    flops = 2 * h_q * (D_QK + D_V) * valid
+    return nbytes, flops
