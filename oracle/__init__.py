@@ -16,6 +16,7 @@ import numpy as np
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "mla_oracle.c"
 _SRC_SPARSE = _HERE / "mla_oracle_sparse.c"
+_SRC_FP8 = _HERE / "mla_oracle_fp8.c"
 _BUILD = _HERE / "_build"
 _LIB = _BUILD / "liboracle.so"
 _lib = None
@@ -23,8 +24,8 @@ _lib = None
 
 def build(force: bool = False, src=None, out: Path = _LIB) -> Path:
     """Compile the oracle with gcc (no GPU code, no HIP headers). src: one C
-    file or a list of them (default: the dense and the sparse decode oracle)."""
-    srcs = [_SRC, _SRC_SPARSE] if src is None else ([src] if isinstance(src, (str, Path)) else list(src))
+    file or a list of them (default: the dense, sparse and FP8 decode oracles)."""
+    srcs = [_SRC, _SRC_SPARSE, _SRC_FP8] if src is None else ([src] if isinstance(src, (str, Path)) else list(src))
     srcs = [Path(x) for x in srcs]
     out.parent.mkdir(parents=True, exist_ok=True)
     if force or not out.exists() or any(out.stat().st_mtime < x.stat().st_mtime for x in srcs):
@@ -56,6 +57,13 @@ def load(path: Path | None = None):
         sp.restype = ctypes.c_int
         sp.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_void_p,
                                                                      ctypes.c_void_p, ctypes.c_int]
+    if hasattr(lib, "mla_oracle_decode_fp8"):
+        f8 = lib.mla_oracle_decode_fp8
+        f8.restype = ctypes.c_int
+        f8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+                                                                     ctypes.c_void_p, ctypes.c_int]
+        lib.mla_oracle_e4m3_value.restype = ctypes.c_double
+        lib.mla_oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     if path is None:
         _lib = lib
     return lib
@@ -134,4 +142,29 @@ def mla_decode_sparse(q, kcache, block_table, indices, counts, softmax_scale, nt
                                       out.ctypes.data, lse.ctypes.data, int(nthreads or default_threads()))
     if rc != 0:
         raise RuntimeError("sparse oracle failed (%d)" % rc)
+    return out, lse
+
+
+def mla_decode_fp8(q, codes, scales, block_table, cache_seqlens, softmax_scale, causal=True,
+                   nthreads: int | None = None, d_v: int = 512, lib=None):
+    """Oracle decode over an FP8 cache: codes uint8 [nblocks, page, d_qk] (E4M3),
+    scales float32 [nblocks, page]; otherwise as mla_decode."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    cache_seqlens = np.ascontiguousarray(cache_seqlens, dtype=np.int32)
+    B, s_q, h_q, d_qk = q.shape
+    nblocks, page, width = codes.shape
+    if width != d_qk or scales.shape != (nblocks, page):
+        raise ValueError("codes must be [nblocks, page, d_qk] and scales [nblocks, page]")
+    out = np.zeros((B, s_q, h_q, d_v), dtype=np.float64)
+    lse = np.zeros((B, s_q, h_q), dtype=np.float64)
+    lib = lib or load()
+    rc = lib.mla_oracle_decode_fp8(q.ctypes.data, codes.ctypes.data, scales.ctypes.data, block_table.ctypes.data,
+                                   cache_seqlens.ctypes.data, B, s_q, h_q, block_table.shape[1], d_qk, d_v, page,
+                                   float(softmax_scale), 1 if causal else 0, out.ctypes.data, lse.ctypes.data,
+                                   int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("fp8 oracle failed (%d)" % rc)
     return out, lse
