@@ -143,10 +143,16 @@ def inp_flops(inp):
 
 
 def bench_append(args, torch, mla, dev):
-    """The cache append alone (mla_append_kv): K launches over replicas of (cache, new rows)."""
+    """The cache append alone: K launches of mla_append_kv (bf16 copy) or, for
+    --op append_fp8, of mla_append_kv_fp8 (quantizing append), over replicas of
+    (cache, new rows)."""
+    fp8 = args.op == "append_fp8"
     inp = wl.make_append()
-    nbytes = wl.append_bytes(inp)
-    rep_bytes = inp.kcache.nbytes + inp.new_rows.nbytes
+    B, s_new, width = inp.new_rows.shape
+    nbytes = wl.append_bytes(inp, fp8=fp8)
+    nblocks = inp.kcache.shape[0]
+    cache_bytes = nblocks * wl.PAGE * (width + 4) if fp8 else inp.kcache.nbytes
+    rep_bytes = cache_bytes + inp.new_rows.nbytes
     R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / rep_bytes))
 
     def bf16(a):
@@ -154,11 +160,20 @@ def bench_append(args, torch, mla, dev):
 
     table = torch.from_numpy(inp.block_table).to(dev)
     lens = torch.from_numpy(inp.cache_seqlens).to(dev)
-    reps = [(bf16(inp.kcache), bf16(inp.new_rows)) for _ in range(R)]
+    if fp8:
+        reps = [(torch.zeros((nblocks, wl.PAGE, width), dtype=torch.uint8, device=dev),
+                 torch.zeros((nblocks, wl.PAGE), dtype=torch.float32, device=dev), bf16(inp.new_rows))
+                for _ in range(R)]
+    else:
+        reps = [(bf16(inp.kcache), bf16(inp.new_rows)) for _ in range(R)]
 
     def step(k):
-        kc, rows = reps[k % R]
-        mla.mla_append_kv(kc, table, lens, rows)
+        if fp8:
+            c, sc, rows = reps[k % R]
+            mla.mla_append_kv_fp8(c, sc, table, lens, rows)
+        else:
+            kc, rows = reps[k % R]
+            mla.mla_append_kv(kc, table, lens, rows)
 
     for k in range(max(args.warmup, R)):
         step(k)
@@ -179,25 +194,34 @@ def bench_append(args, torch, mla, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     gbs = nbytes / (ms * 1e-3) / 1e9
-    B, s_new = inp.new_rows.shape[:2]
+    kname = "append_fp8_kernel (mla_append_kv_fp8)" if fp8 else "append_kernel (mla_append_kv)"
     result = {
-        "metric": "MLA cache append HBM GB/s (fraction of MI355X peak), paged bf16",
+        "metric": "MLA cache append HBM GB/s (fraction of MI355X peak), paged %s"
+                  % ("FP8 (E4M3 + per-row scale) from bf16 rows" if fp8 else "bf16"),
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "append: " + wl.APPEND_DESCRIPTION + ", row 576 bf16, block 64, shuffled block_table",
+        "dtype": "bf16 in, fp8e4m3 + f32 scale out" if fp8 else "bf16", "data": "synthetic",
+        "config": {"workload": "append%s: %s, row 576, block 64, shuffled block_table"
+                               % ("_fp8" if fp8 else "", wl.APPEND_DESCRIPTION),
                    "batch": int(B), "s_new": int(s_new), "replicas": R},
         "alg_bytes_per_step": nbytes,
-        "roofline": {"bound": "hbm", "kernel": "append_kernel (mla_append_kv)", "achieved": round(gbs, 2),
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel_ms_avg": round(ms, 6)},
     }
     if not args.no_cpu_baseline:
         from oracle import append as oracle_append
+        from oracle import fp8 as oracle_fp8
+        if fp8:
+            c0 = np.zeros((nblocks, wl.PAGE, width), dtype=np.uint8)
+            s0 = np.zeros((nblocks, wl.PAGE), dtype=np.float32)
         t0 = time.perf_counter()
         n = 0
         while True:
-            oracle_append.append_rows(inp.kcache, inp.block_table, inp.cache_seqlens, inp.new_rows)
+            if fp8:
+                oracle_fp8.append_rows_fp8(c0, s0, inp.block_table, inp.cache_seqlens, inp.new_rows)
+            else:
+                oracle_append.append_rows(inp.kcache, inp.block_table, inp.cache_seqlens, inp.new_rows)
             n += 1
             if time.perf_counter() - t0 >= min(args.cpu_seconds, 10.0) or n >= 50:
                 break
@@ -294,6 +318,103 @@ def bench_sparse(args, torch, mla, dev):
     return 0
 
 
+def bench_fp8(args, torch, mla, dev):
+    """Decode over the FP8 cache: plan (mla_get_metadata_fp8) + mla_decode_fp8_fwd per step.
+    The cache is the named workload's bf16 cache, quantized on the GPU by mla_append_kv_fp8
+    (each sequence appended whole), then copied into R replicas."""
+    inp = wl.make_workload(args.workload, poison=False)
+    B, s_q, h_q = inp.batch, inp.s_q, inp.h_q
+    nbytes, flops = wl.fp8_counts(inp.cache_seqlens, s_q, h_q, inp.causal)
+    nblocks = inp.kcache.shape[0]
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    table = torch.from_numpy(inp.block_table).to(dev)
+    lens = torch.from_numpy(inp.cache_seqlens).to(dev)
+    codes0 = torch.zeros((nblocks, wl.PAGE, wl.D_QK), dtype=torch.uint8, device=dev)
+    scales0 = torch.zeros((nblocks, wl.PAGE), dtype=torch.float32, device=dev)
+    mla.mla_append_kv_fp8(codes0, scales0, table, lens, bf16(wl.rows_in_token_order(inp)))
+    torch.cuda.synchronize()
+    rep_bytes = codes0.numel() + 4 * scales0.numel() + inp.q.nbytes + inp.block_table.nbytes
+    R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / rep_bytes))
+    q0 = bf16(inp.q)
+    reps = [(codes0.clone(), scales0.clone(), q0.clone(), table.clone(), lens.clone()) for _ in range(R)]
+    del codes0, scales0, q0
+    sizes = mla.mla_fp8_plan_sizes(B, s_q, h_q)
+    units = sizes["num_units"]
+    plans = [(torch.empty((units, mla.META_INTS), dtype=torch.int32, device=dev),
+              torch.empty((B + 1,), dtype=torch.int32, device=dev)) for _ in range(R)]
+    out = torch.empty((B, s_q, h_q, mla.D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(sizes["workspace_bytes"], 16),), dtype=torch.uint8, device=dev)
+
+    def step(k):
+        c, sc, q, tab, ln = reps[k % R]
+        meta, splits = plans[k % R]
+        mla.mla_get_metadata_fp8(ln, h_q, s_q, num_units=units, tile_meta=meta, num_splits=splits)
+        mla.mla_decode_fp8_fwd(q, c, sc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal, out=out,
+                               lse=lse, workspace=ws)
+
+    for k in range(max(args.warmup, R)):
+        step(k)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for k in range(args.steps):
+            step(k)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "MLA decode over an FP8 (E4M3 + per-row scale) paged latent cache, HBM GB/s + TFLOPS",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 cache, bf16 query/output, f32 accumulate", "data": "synthetic",
+        "config": {"workload": "fp8 %s: %s, cache quantized per row (E4M3, f32 scale), d_qk=576, d_v=512, block 64, "
+                               "shuffled block_table, scale 1/sqrt(192)"
+                               % (args.workload, wl.DESCRIPTIONS[args.workload]),
+                   "batch": B, "s_q": s_q, "h_q": h_q, "tokens": int(inp.cache_seqlens.sum()), "replicas": R,
+                   "num_units": units},
+        "tflops": round(tf, 3), "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
+        "roofline": {"bound": "hbm", "kernel": "fp8 decode step (plan + decode + combine)", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_ms_avg": round(ms, 6)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        from oracle import fp8 as ofp8
+        nth = orc.default_threads()
+        codes, scales = ofp8.quantize_rows(inp.kcache)
+        sample = [0, 1]
+        sub = wl.subset(inp, sample)
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            orc.mla_decode_fp8(sub.q, codes, scales, sub.block_table, sub.cache_seqlens, inp.softmax_scale,
+                               inp.causal, nthreads=nth)
+            n += 1
+            if time.perf_counter() - t0 >= min(args.cpu_seconds, 10.0) or n >= 20:
+                break
+        sec = (time.perf_counter() - t0) / n
+        sub_bytes = wl.fp8_counts(sub.cache_seqlens, s_q, h_q, inp.causal)[0]
+        result["cpu_baseline"] = {"value": round(sub_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": nth,
+                                  "kind": "oracle",
+                                  "sample": "%d passes over sequences %s of the batch" % (n, sample)}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,9 +430,10 @@ def main(argv=None):
                     help="no GPU: write the workload's HBM bytes per decode launch to profiles/decode_traffic.json "
                          "from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv outputs")
     ap.add_argument("--copy-bytes", type=int, default=256 * 2 ** 20, help="size of the calibration copy")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "sparse"],
-                    help="decode: the hot path (default); append: the cache-append kernel alone; "
-                         "sparse: top-k index decode (plan + decode + combine)")
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "append_fp8", "sparse", "fp8"],
+                    help="decode: the hot path (default); append / append_fp8: the cache-append kernel alone "
+                         "(bf16 copy / quantizing FP8 append); sparse: top-k index decode (plan + decode + "
+                         "combine); fp8: decode over the FP8 cache of --workload")
     args = ap.parse_args(argv)
     if args.pmc_summary:
         return pmc_summary(args)
@@ -340,8 +462,10 @@ def main(argv=None):
         return 0
 
     mla.load_library()
-    if args.op == "append":
+    if args.op in ("append", "append_fp8"):
         return bench_append(args, torch, mla, dev)
+    if args.op == "fp8":
+        return bench_fp8(args, torch, mla, dev)
     if args.op == "sparse":
         return bench_sparse(args, torch, mla, dev)
     inp = wl.make_workload(args.workload, poison=False)

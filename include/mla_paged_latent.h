@@ -218,6 +218,44 @@ int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks,
                           void* stream);
 
 /*
+ * FP8 latent cache: cached rows stored as 8-bit floats with one float32 scale
+ * per row, half the bytes of the bf16 cache -- the FP8 support the FlashMLA
+ * explainer (theflyingbirds.in) lists under section 9, "Future Directions",
+ * to cut memory further. The pages fix no format; this library uses:
+ *   codes: uint8 [nblocks, 64, 576], OCP E4M3 (sign, 4 exponent bits with
+ *     bias 7, 3 mantissa bits, subnormals, no infinities, 0x7F/0xFF NaN);
+ *   scales: float32 [nblocks, 64]; cached value = E4M3(code) * scale.
+ * The attention is that of mla_decode_fwd over the decoded values (queries
+ * stay bf16); rows no query may read may hold anything, NaN included.
+ *
+ * mla_fp8_plan_sizes / mla_get_metadata_fp8: the plan for this decode (its
+ *   kernel handles 16 query rows per workgroup for every s_q*h_q), same
+ *   arguments and outputs as mla_plan_sizes / mla_get_metadata.
+ * mla_decode_fp8_fwd: as mla_decode_fwd with kcache replaced by (kcodes,
+ *   kscale); both 16-byte aligned.
+ * mla_append_kv_fp8: as mla_append_kv, but each new bf16 row is quantized
+ *   into the FP8 cache: amax = its largest magnitude, scale = amax / 448 and
+ *   code = E4M3 nearest (ties to even) to x * (448 / amax), the two quotients
+ *   correctly rounded float32 and the product one float32 multiply; a row of
+ *   zeros gets scale 0 and codes 0. Rows must be finite. kcodes 16-byte and
+ *   kscale 4-byte aligned.
+ * Errors: as for the bf16 calls.
+ */
+int mla_fp8_plan_sizes(int batch, int s_q, int h_q, int num_cus, int* num_units,
+                       size_t* meta_bytes, size_t* splits_bytes, size_t* workspace_bytes);
+int mla_get_metadata_fp8(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_units,
+                         int32_t* tile_meta, int32_t* num_splits, void* stream);
+int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, int64_t nblocks,
+                       const int32_t* block_table, int max_blocks,
+                       const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                       float softmax_scale, int causal,
+                       const int32_t* tile_meta, const int32_t* num_splits, int num_units,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int mla_append_kv_fp8(void* kcodes, float* kscale, int64_t nblocks, const int32_t* block_table, int max_blocks,
+                      const int32_t* cache_seqlens, const void* new_rows, int batch, int s_new, void* stream);
+
+/*
  * Cache append: writes the new tokens' cached rows into their blocks, the
  * step that precedes decode attention over them (the cache grows by the new
  * tokens' entries each step: "OpenSourceWeek Day 1: FlashMLA", "How KV

@@ -68,6 +68,16 @@ def load_library(path: Path | str | None = None):
     lib.mla_decode_sparse_fwd.restype = i32
     lib.mla_decode_sparse_fwd.argtypes = [vp, vp, i64, vp, i32, vp, vp, i32, i32, i32, i32, ctypes.c_float,
                                           vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.mla_fp8_plan_sizes.restype = i32
+    lib.mla_fp8_plan_sizes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(sz),
+                                       ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.mla_get_metadata_fp8.restype = i32
+    lib.mla_get_metadata_fp8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_decode_fp8_fwd.restype = i32
+    lib.mla_decode_fp8_fwd.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, i32,
+                                       vp, vp, vp, sz, vp]
+    lib.mla_append_kv_fp8.restype = i32
+    lib.mla_append_kv_fp8.argtypes = [vp, vp, i64, vp, i32, vp, vp, i32, i32, vp]
     lib.mla_append_kv.restype = i32
     lib.mla_append_kv.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, vp]
     lib.mla_block_pool_create.restype = i32
@@ -325,6 +335,101 @@ def mla_decode_sparse_fwd(q, kcache, block_table, indices, topk_lens, softmax_sc
     return out, lse
 
 
+def mla_fp8_plan_sizes(batch: int, s_q: int, h_q: int, num_cus: int = 0) -> dict:
+    """Plan geometry and buffer sizes for the FP8-cache decode (host only)."""
+    units = ctypes.c_int(0)
+    meta, splits, ws = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mla_fp8_plan_sizes", load_library().mla_fp8_plan_sizes(batch, s_q, h_q, num_cus, ctypes.byref(units),
+                                                                    ctypes.byref(meta), ctypes.byref(splits),
+                                                                    ctypes.byref(ws)))
+    return {"num_units": units.value, "meta_bytes": meta.value, "splits_bytes": splits.value,
+            "workspace_bytes": ws.value}
+
+
+def mla_get_metadata_fp8(cache_seqlens, h_q: int, s_q: int = 1, num_units: int | None = None, tile_meta=None,
+                         num_splits=None):
+    """Split plan for the FP8-cache decode (device). Returns (tile_meta, num_splits)."""
+    import torch
+    _need(cache_seqlens, torch.int32, "cache_seqlens")
+    B = int(cache_seqlens.shape[0])
+    dev = cache_seqlens.device
+    with _on(torch, dev):
+        if num_units is None:
+            num_units = mla_fp8_plan_sizes(B, s_q, h_q)["num_units"]
+        if tile_meta is None:
+            tile_meta = torch.empty((num_units, META_INTS), dtype=torch.int32, device=dev)
+        if num_splits is None:
+            num_splits = torch.empty((B + 1,), dtype=torch.int32, device=dev)
+        _check("mla_get_metadata_fp8", load_library().mla_get_metadata_fp8(
+            cache_seqlens.data_ptr(), B, s_q, h_q, num_units, tile_meta.data_ptr(), num_splits.data_ptr(),
+            _stream(torch)))
+    return tile_meta, num_splits
+
+
+def mla_decode_fp8_fwd(q, kcodes, kscale, block_table, cache_seqlens, softmax_scale: float, tile_meta, num_splits,
+                       causal: bool = True, out=None, lse=None, workspace=None):
+    """Decode over an FP8 cache: kcodes uint8 [nblocks, 64, 576] (E4M3), kscale float32
+    [nblocks, 64]; the rest as mla_decode_fwd. Returns (out, lse)."""
+    import torch
+    _need(q, torch.bfloat16, "q")
+    dev = q.device
+    _need(kcodes, torch.uint8, "kcodes", dev)
+    _need(kscale, torch.float32, "kscale", dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    _need(cache_seqlens, torch.int32, "cache_seqlens", dev)
+    _need(tile_meta, torch.int32, "tile_meta", dev)
+    _need(num_splits, torch.int32, "num_splits", dev)
+    if q.dim() != 4 or q.shape[3] != D_QK:
+        raise ValueError("q must be [B, s_q, h_q, 576]")
+    if kcodes.dim() != 3 or kcodes.shape[1] != PAGE_SIZE or kcodes.shape[2] != D_QK:
+        raise ValueError("kcodes must be [nblocks, 64, 576]")
+    if tuple(kscale.shape) != tuple(kcodes.shape[:2]):
+        raise ValueError("kscale must be [nblocks, 64]")
+    B, s_q, h_q, _ = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and cache_seqlens [B]")
+    num_units = int(tile_meta.shape[0])
+    with _on(torch, dev):
+        if out is None:
+            out = torch.empty((B, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+        if workspace is None:
+            ws = max(mla_fp8_plan_sizes(B, s_q, h_q)["workspace_bytes"], workspace_bytes(B, s_q, h_q, num_units))
+            workspace = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
+        _check("mla_decode_fp8_fwd", load_library().mla_decode_fp8_fwd(
+            q.data_ptr(), kcodes.data_ptr(), kscale.data_ptr(), int(kcodes.shape[0]), block_table.data_ptr(),
+            int(block_table.shape[1]), cache_seqlens.data_ptr(), B, s_q, h_q, float(softmax_scale),
+            1 if causal else 0, tile_meta.data_ptr(), num_splits.data_ptr(), num_units, out.data_ptr(),
+            lse.data_ptr(), workspace.data_ptr(), int(workspace.numel()), _stream(torch)))
+    return out, lse
+
+
+def mla_append_kv_fp8(kcodes, kscale, block_table, cache_seqlens, new_rows):
+    """FP8 cache append: quantize new_rows bf16 [B, s_new, 576] into (kcodes, kscale) at
+    positions cache_seqlens[b] - s_new + i. Updates both in place and returns them."""
+    import torch
+    _need(kcodes, torch.uint8, "kcodes")
+    dev = kcodes.device
+    _need(kscale, torch.float32, "kscale", dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    _need(cache_seqlens, torch.int32, "cache_seqlens", dev)
+    _need(new_rows, torch.bfloat16, "new_rows", dev)
+    if kcodes.dim() != 3 or kcodes.shape[1] != PAGE_SIZE or kcodes.shape[2] != D_QK or \
+            tuple(kscale.shape) != tuple(kcodes.shape[:2]):
+        raise ValueError("kcodes must be [nblocks, 64, 576] and kscale [nblocks, 64]")
+    if new_rows.dim() != 3 or new_rows.shape[2] != D_QK:
+        raise ValueError("new_rows must be [B, s_new, 576]")
+    B, s_new = int(new_rows.shape[0]), int(new_rows.shape[1])
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and cache_seqlens [B]")
+    with _on(torch, dev):
+        _check("mla_append_kv_fp8", load_library().mla_append_kv_fp8(
+            kcodes.data_ptr(), kscale.data_ptr(), int(kcodes.shape[0]), block_table.data_ptr(),
+            int(block_table.shape[1]), cache_seqlens.data_ptr(), new_rows.data_ptr(), B, s_new, _stream(torch)))
+    return kcodes, kscale
+
+
 def mla_append_kv(kcache, block_table, cache_seqlens, new_rows):
     """Cache append: new_rows bf16 [B, s_new, 576] go to token positions
     cache_seqlens[b] - s_new + i of their sequence (cache_seqlens counts them).
@@ -404,5 +509,6 @@ def workspace_bytes(batch: int, s_q: int, h_q: int, num_units: int) -> int:
 __all__ = ["mla_plan_sizes", "mla_workspace_bytes", "mla_get_metadata", "mla_get_metadata_host", "mla_decode_fwd",
            "mla_decode_fwd_splits", "mla_combine_splits", "mla_append_kv", "BlockPool",
            "mla_sparse_plan_sizes", "mla_get_metadata_sparse", "mla_decode_sparse_fwd",
+           "mla_fp8_plan_sizes", "mla_get_metadata_fp8", "mla_decode_fp8_fwd", "mla_append_kv_fp8",
            "workspace_bytes", "load_library", "status_string", "MLAError", "LIB_PATH",
            "D_QK", "D_V", "PAGE_SIZE", "META_INTS"]

@@ -13,6 +13,7 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_u
 hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_decode_sparse(const DecodeParams& p, int num_units, int head_groups, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeParams& p, int num_units, int head_groups, hipStream_t stream);
 }  // namespace mla
 
 namespace {
@@ -189,6 +190,7 @@ int setup_decode(const void* q, const void* kcache, int64_t nblocks, const int32
     p->indices = nullptr;
     p->topk = 0;
     p->sq_real = 1;
+    p->kscale = nullptr;
     *geo_out = geo;
     return MLA_OK;
 }
@@ -371,8 +373,101 @@ int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks, co
     p.indices = indices;
     p.topk = topk;
     p.sq_real = s_q;
+    p.kscale = nullptr;
     hipStream_t st = (hipStream_t)stream;
     if (mla::launch_decode_sparse(p, num_units, h_q / 16, st) != hipSuccess) return MLA_ERR_HIP;
+    return run_combine(p, st);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- FP8 cache decode
+//
+// The FP8 cache is decoded by the 16-row streaming kernel for every s_q*h_q,
+// so its plan is always the per-sequence plan.
+
+extern "C" {
+
+int mla_fp8_plan_sizes(int batch, int s_q, int h_q, int num_cus, int* num_units, size_t* meta_bytes,
+                       size_t* splits_bytes, size_t* workspace_bytes)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (num_cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+        if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return MLA_ERR_HIP;
+        if (num_cus <= 0) return MLA_ERR_HIP;
+    }
+    const int rows = s_q * h_q;
+    int units = num_cus / (rows / 16);
+    if (units < batch + 1) units = batch + 1;
+    size_t part_o = 0, total = 0;
+    workspace_layout(batch, rows, units, &part_o, &total);
+    if (num_units) *num_units = units;
+    if (meta_bytes) *meta_bytes = (size_t)units * mla::kMetaInts * sizeof(int32_t);
+    if (splits_bytes) *splits_bytes = (size_t)(batch + 1) * sizeof(int32_t);
+    if (workspace_bytes) *workspace_bytes = total;
+    return MLA_OK;
+}
+
+int mla_get_metadata_fp8(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_units,
+                         int32_t* tile_meta, int32_t* num_splits, void* stream)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (!cache_seqlens || !tile_meta || !num_splits || num_units < batch + 1) return MLA_ERR_INVALID_ARG;
+    if (mla::launch_plan(cache_seqlens, batch, 16, num_units, tile_meta, num_splits, (hipStream_t)stream) !=
+        hipSuccess)
+        return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, int64_t nblocks,
+                       const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch, int s_q,
+                       int h_q, float softmax_scale, int causal, const int32_t* tile_meta, const int32_t* num_splits,
+                       int num_units, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = check_shape(batch, s_q, h_q);
+    if (rc != MLA_OK) return rc;
+    if (!q || !kcodes || !kscale || !block_table || !cache_seqlens || !tile_meta || !num_splits || !out || !lse ||
+        !workspace)
+        return MLA_ERR_INVALID_ARG;
+    if (nblocks < 1 || max_blocks < 1 || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kcodes) || !aligned16(kscale) || !aligned16(out) || !aligned16(workspace) ||
+        ((uintptr_t)lse & 3u))
+        return MLA_ERR_INVALID_ARG;
+    if (num_units < batch + 1) return MLA_ERR_INVALID_ARG;
+    const int rows = s_q * h_q;
+    size_t part_o = 0, total = 0;
+    workspace_layout(batch, rows, num_units, &part_o, &total);
+    if (workspace_bytes < total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    mla::DecodeParams p;
+    p.q = (const uint16_t*)q;
+    p.kcache = (const uint16_t*)kcodes;
+    p.block_table = block_table;
+    p.seqlens = cache_seqlens;
+    p.meta = tile_meta;
+    p.splits = num_splits;
+    p.out = (uint16_t*)out;
+    p.lse = lse;
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)((char*)workspace + part_o);
+    p.nblocks = nblocks;
+    p.max_blocks = max_blocks;
+    p.batch = batch;
+    p.s_q = s_q;
+    p.h_q = h_q;
+    p.rows_total = rows;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.indices = nullptr;
+    p.topk = 0;
+    p.sq_real = 1;
+    p.kscale = kscale;
+    hipStream_t st = (hipStream_t)stream;
+    if (mla::launch_decode_fp8(p, num_units, rows / 16, st) != hipSuccess) return MLA_ERR_HIP;
     return run_combine(p, st);
 }
 

@@ -25,6 +25,7 @@ namespace mla {
 namespace {
 
 typedef unsigned u32x4a __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2a __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(256) void append_kernel(uint16_t* __restrict__ kcache,
                                                      const int32_t* __restrict__ block_table, int max_blocks,
@@ -46,6 +47,57 @@ __global__ __launch_bounds__(256) void append_kernel(uint16_t* __restrict__ kcac
     if (lane < 8) c = src[64 + lane];
     dst[lane] = a;
     if (lane < 8) dst[64 + lane] = c;
+}
+
+// FP8 append: one wave per new row. Lanes 0-63 hold bf16 columns 8l..8l+7 and
+// lanes 0-7 also 512+8l..; the row's largest magnitude comes from a wave max;
+// scale = amax / 448 and codes = E4M3(x * (448 / amax)), both quotients
+// correctly rounded float32 and the product one float32 multiply, converted
+// to E4M3 by the hardware (round to nearest even; |x * 448 / amax| <= 448 so
+// nothing saturates). A zero row gets scale 0 and codes 0.
+__global__ __launch_bounds__(256) void append_fp8_kernel(unsigned char* __restrict__ codes, float* __restrict__ scales,
+                                                         const int32_t* __restrict__ block_table, int max_blocks,
+                                                         const int32_t* __restrict__ seqlens,
+                                                         const uint16_t* __restrict__ rows, int batch, int s_new)
+{
+    const int lane = threadIdx.x & 63;
+    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= (long)batch * s_new) return;
+    const int b = (int)(r / s_new);
+    const int i = (int)(r - (long)b * s_new);
+    const int pos = seqlens[b] - s_new + i;
+    if (pos < 0) return;
+    const int page = block_table[(size_t)b * max_blocks + (pos >> 6)];
+    const size_t drow = (size_t)page * kPage + (pos & (kPage - 1));
+    const u32x4a* src = (const u32x4a*)(rows + (size_t)r * kDqk);
+    const u32x4a a = src[lane];
+    u32x4a c = {0u, 0u, 0u, 0u};
+    if (lane < 8) c = src[64 + lane];
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(a[k] << 16);
+        x[2 * k + 1] = __uint_as_float(a[k] & 0xFFFF0000u);
+        x[8 + 2 * k] = __uint_as_float(c[k] << 16);
+        x[8 + 2 * k + 1] = __uint_as_float(c[k] & 0xFFFF0000u);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(x[k]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float inv = m > 0.f ? __fdiv_rn(448.f, m) : 0.f;
+    unsigned w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k] * inv, x[4 * k + 1] * inv, 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k + 2] * inv, x[4 * k + 3] * inv, v, true);
+        w[k] = (unsigned)v;
+    }
+    unsigned* dst = (unsigned*)(codes + drow * kDqk);
+    *(u32x2a*)(dst + 2 * lane) = u32x2a{w[0], w[1]};
+    if (lane < 8) *(u32x2a*)(dst + 128 + 2 * lane) = u32x2a{w[2], w[3]};
+    if (lane == 0) scales[drow] = m > 0.f ? __fdiv_rn(m, 448.f) : 0.f;
 }
 
 struct BlockPool {
@@ -75,6 +127,20 @@ int mla_append_kv(void* kcache, int64_t nblocks, const int32_t* block_table, int
     const dim3 grid((unsigned)((rows + 3) / 4));
     hipLaunchKernelGGL(mla::append_kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint16_t*)kcache, block_table,
                        max_blocks, cache_seqlens, (const uint16_t*)new_rows, batch, s_new);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_append_kv_fp8(void* codes, float* scales, int64_t nblocks, const int32_t* block_table, int max_blocks,
+                      const int32_t* cache_seqlens, const void* new_rows, int batch, int s_new, void* stream)
+{
+    if (!codes || !scales || !block_table || !cache_seqlens || !new_rows) return MLA_ERR_INVALID_ARG;
+    if (nblocks < 1 || max_blocks < 1 || batch < 1 || s_new < 1) return MLA_ERR_INVALID_ARG;
+    if (!mla::aligned16(codes) || !mla::aligned16(new_rows) || ((uintptr_t)scales & 3u)) return MLA_ERR_INVALID_ARG;
+    const long rows = (long)batch * s_new;
+    if (rows > (long)0x7fffffff * 4 - 4) return MLA_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    hipLaunchKernelGGL(mla::append_fp8_kernel, grid, dim3(256), 0, (hipStream_t)stream, (unsigned char*)codes,
+                       scales, block_table, max_blocks, cache_seqlens, (const uint16_t*)new_rows, batch, s_new);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -115,6 +115,9 @@ struct DecodeParams {
     const int32_t* indices;
     int topk;
     int sq_real;
+    // FP8 decode only: kcache holds E4M3 codes [nblocks, 64, 576] and kscale
+    // the float32 scale of each cached row [nblocks, 64]
+    const float* kscale;
 };
 
 struct CombineParams {

@@ -68,11 +68,91 @@ __device__ __forceinline__ void copy_rows(const unsigned char* gbase, int valid,
     }
 }
 
-// ---------------------------------------------------------------- streaming kernel
-
 constexpr int kSlotA = 19 * 1024;        // 16 rows x 1168 B, rounded up to whole 1 KB copies
 constexpr int kDmaA = 19;
 constexpr int kLdsA = 8 * kSlotA;        // two slots per wave: 155,648 B
+
+// Merge the four waves' (m, l, O) of a 16-row streaming workgroup and write
+// the result. Wave w owns output tiles nt in [8w, 8w + 8) (dims [128w,
+// 128w + 128)) and keeps them in registers. As soon as it is done with its
+// slots it posts its other 24 tiles (unscaled, bf16) and its running max/sum
+// per row into its own slot area; one workgroup barrier later every wave folds
+// in the others' tiles. acc[nt] element i is dim 16 nt + 4 (lane / 16) + i of
+// row lane % 16 of the workgroup's rows.
+__device__ __forceinline__ void stream_merge_store(const DecodeParams& p, const f32x4* acc, float mrun_, float lrun_,
+                                                   unsigned lds0, unsigned slot0, int wave, int lane, int b, int slot,
+                                                   int nsplit)
+{
+    constexpr int R = 16;
+    const int g = lane >> 4;
+    const int c16 = lane & 15;
+    f32x4 accl[32];
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) accl[nt] = acc[nt];
+    float mrun[1] = {mrun_}, lrun[1] = {lrun_};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");       // this wave's slot reads are done
+    {
+        const unsigned mine = slot0;
+        if (g == 0) {
+            *(lds_f32*)(uintptr_t)(mine + 16384u + 4u * c16) = mrun[0];
+            *(lds_f32*)(uintptr_t)(mine + 16384u + 64u + 4u * c16) = lrun[0];
+        }
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) {
+            if ((nt >> 3) == wave) continue;
+            const u32x2 v = {pack_bf16x2(accl[nt][0], accl[nt][1]), pack_bf16x2(accl[nt][2], accl[nt][3])};
+            *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(mine + (unsigned)((nt * 64 + lane) * 8)) = v;
+        }
+    }
+    wg_barrier();
+    {
+        float mw[4], mall = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            mw[w] = *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 4u * c16);
+            mall = fmaxf(mall, mw[w]);
+        }
+        float fw[4], lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            fw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mall);
+            lt += *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 64u + 4u * c16) * fw[w];
+        }
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int grow = blockIdx.y * R + c16;
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) {
+            if ((nt >> 3) != wave) continue;                  // static tile index, uniform branch
+            f32x4 v = accl[nt] * fw[nt >> 3];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                if (w == wave) continue;
+                const u32x2 o = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(
+                    lds0 + (unsigned)(2 * w) * kSlotA + (unsigned)((nt * 64 + lane) * 8));
+                v[0] += __uint_as_float(o[0] << 16) * fw[w];
+                v[1] += __uint_as_float(o[0] & 0xFFFF0000u) * fw[w];
+                v[2] += __uint_as_float(o[1] << 16) * fw[w];
+                v[3] += __uint_as_float(o[1] & 0xFFFF0000u) * fw[w];
+            }
+            v *= inv;
+            const int d = 16 * nt + 4 * g;
+            if (nsplit == 1) {
+                const u32x2 ob = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                *(u32x2*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = ob;
+            } else {
+                *(f32x4*)(p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d) = v;
+            }
+        }
+        if (wave == 0 && g == 0) {
+            const float lse = lt > 0.f ? (mall + __log2f(lt)) * kLn2 : -INFINITY;
+            if (nsplit == 1) p.lse[(size_t)b * p.rows_total + grow] = lse;
+            else p.part_lse[(size_t)slot * p.rows_total + grow] = lse;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- streaming kernel
+
 constexpr int kMaxTopk = 2048;           // sparse decode: longest token list
 constexpr int kRowTabB = kMaxTopk * 4;   // sparse decode: cache row of each listed token of the unit
 
@@ -279,70 +359,227 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
         }
     }
 
-    // ---- merge the four waves' (m, l, O) and write the result. Wave w owns
-    // output tiles nt in [8w, 8w + 8) (dims [128w, 128w + 128)) and keeps them
-    // in registers. As soon as it is done with its slots it posts its other 24
-    // tiles (unscaled, bf16) and its running max/sum per row into its own slot
-    // area; one workgroup barrier later every wave folds in the others' tiles.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");       // this wave's slot reads are done
-    {
-        const unsigned mine = slot0;
-        if (g == 0) {
-            *(lds_f32*)(uintptr_t)(mine + 16384u + 4u * c16) = mrun[0];
-            *(lds_f32*)(uintptr_t)(mine + 16384u + 64u + 4u * c16) = lrun[0];
-        }
+    stream_merge_store(p, acc[0], mrun[0], lrun[0], lds0, slot0, wave, lane, b, slot, nsplit);
+}
+
+// ---------------------------------------------------------------- FP8 streaming kernel
+//
+// The streaming kernel over an FP8 cache (E4M3 codes, one float32 scale per
+// cached row). A sub-tile is 32 tokens (32 x 576 code bytes: the same LDS
+// footprint as 16 bf16 rows), so that the PV product can take 32 tokens per
+// v_mfma_f32_16x16x32_bf16. Codes are turned into bf16 exactly (every E4M3
+// value is a bf16 value) right before the matrix ops; the row scales are
+// applied to the scores (S_t * scale_t) and to P (P_t * scale_t before PV), so
+// they never touch the matrix operands.
+//
+// Slot layout (19 KB, 1216 chunks of 16 B): rows 0-15 at chunk 37 r, rows 16-31
+// at 37 r + 1 (576 B of codes + one pad chunk; the extra chunk keeps rows r
+// and r + 16 in different banks for the transpose reads), then the 32 row
+// scales at chunk 1185. K rows are read 8 bytes per lane (ds_read_b64); V^T
+// comes from ds_read_b64_tr_b8: in each 16-lane group, output lane j byte e is
+// byte j % 8 of source lane 2e + j / 8, so source lane 2e + p reads dims
+// [16 dt + 8 p, +8) of token T(G, e) and output lane j gets dim 16 dt + j of
+// the 8 tokens T(G, 0..7) -- the A operand of the 16x16x32 product.
+
+constexpr int kF8Chunks = 37;                        // chunks per LDS row: 36 of codes + 1 pad
+constexpr int kF8Row16 = 16 * kF8Chunks + 1;         // chunk position of row 16
+constexpr int kF8Scale = 2 * 16 * kF8Chunks + 1;     // chunk position of the 32 row scales
+
+__device__ __forceinline__ unsigned f8_row(int r) { return 16u * (unsigned)(kF8Chunks * r + (r >> 4)); }
+
+// token (0..31 within the sub-tile) of element e of a lane of group g in the
+// S^T tiles / P^T operand: elements 0-3 are tile 0 rows 4g..4g+3, 4-7 tile 1
+__device__ __forceinline__ int f8_token(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw)
+{
+    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.f, false);
+    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.f, true);
+    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.f, false);
+    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.f, true);
+    return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+__global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsA];
+    const unsigned lds0 = lds_base(smem);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int c16 = lane & 15;
+
+    const i32x8 meta = sload8(p.meta + (size_t)blockIdx.x * kMetaInts);
+    const int b = meta[0];
+    const int j0 = meta[1];
+    const int j1 = meta[3];
+    const int L = meta[5];
+    const int slot = meta[6];
+    const int nsplit = meta[7];
+    if (b >= p.batch || j0 >= j1) return;
+    const int tok_begin = j0 * kPage;
+    const int tok_end = min(j1 * kPage, L);
+    const int nsub = (tok_end - tok_begin + 31) >> 5;
+    const int K = nsub > wave ? (nsub - wave + 3) >> 2 : 0;   // this wave's sub-tiles: wave, wave+4, ...
+    const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
+    const int npages = j1 - j0;
+    const int page_vec = lane < npages ? table[j0 + lane] : 0;
+    const unsigned char* codes = (const unsigned char*)p.kcache;
+
+    float mrun = -INFINITY, lrun = 0.f;
+    f32x4 acc[32];
 #pragma unroll
-        for (int nt = 0; nt < 32; ++nt) {
-            if ((nt >> 3) == wave) continue;
-            const u32x2 v = {pack_bf16x2(acc[0][nt][0], acc[0][nt][1]), pack_bf16x2(acc[0][nt][2], acc[0][nt][3])};
-            *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(mine + (unsigned)((nt * 64 + lane) * 8)) = v;
+    for (int nt = 0; nt < 32; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const unsigned slot0 = lds0 + (unsigned)(2 * wave) * kSlotA;
+    auto issue = [&](int k) {
+        const int tok = tok_begin + 32 * (wave + 4 * k);
+        const int pidx = (tok >> 6) - j0;
+        const int page = pidx < 64 ? __builtin_amdgcn_readlane(page_vec, pidx) : sload(table + j0 + pidx);
+        const size_t row0 = (size_t)page * kPage + (size_t)(tok & 63);
+        const unsigned char* gbase = codes + row0 * kDqk;
+        const unsigned char* sbase = (const unsigned char*)(p.kscale + row0);
+        const int valid = min(32, tok_end - tok);
+        const unsigned dst = slot0 + (unsigned)(k & 1) * kSlotA;
+        for (int i = 0; i < kDmaA; ++i) {
+            const int pos = i * 64 + lane;
+            const unsigned char* src = gbase;                  // pad chunks: any in-bounds bytes
+            if (pos < kF8Scale) {
+                const int hb = pos >= 16 * kF8Chunks;
+                const int pp = hb ? pos - kF8Row16 : pos;
+                if (pp >= 0) {
+                    const int r = pp / kF8Chunks;
+                    const int c = pp - r * kF8Chunks;
+                    const int rr = 16 * hb + r;
+                    if (c < 36) src = gbase + (size_t)(rr < valid ? rr : 0) * kDqk + 16 * c;
+                }
+            } else if (pos < kF8Scale + 8) {
+                src = sbase + 16 * (pos - kF8Scale);
+            }
+            dma16(src, dst + (unsigned)i * 1024u);
         }
+    };
+
+    // Prologue (as in the bf16 streaming kernel): the queries go through LDS
+    // (wave 3's second slot), so that every later wait is for copies only.
+    const unsigned qslot = lds0 + 7u * kSlotA;
+    const unsigned char* qbase = (const unsigned char*)(p.q + ((size_t)b * p.rows_total + blockIdx.y * 16) * kDqk);
+    settle_loads();
+    if (K > 0) issue(0);
+    copy_rows(qbase, 16, qslot, wave, 4, kDmaA, lane);
+    if (wave < 3 && K > 1) {
+        issue(1);
+        MLA_WAIT_VM(19);
+    } else {
+        MLA_WAIT_VM(0);
     }
     wg_barrier();
+    bf16x8 qf[18];
     {
-        float mw[4], mall = -INFINITY;
+        const unsigned qa = qslot + (unsigned)(c16 * kLdsRow + 16 * g);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            mw[w] = *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 4u * c16);
-            mall = fmaxf(mall, mw[w]);
-        }
-        float fw[4], lt = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            fw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mall);
-            lt += *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 64u + 4u * c16) * fw[w];
-        }
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int grow = blockIdx.y * R + c16;
-#pragma unroll
-        for (int nt = 0; nt < 32; ++nt) {
-            if ((nt >> 3) != wave) continue;                  // static tile index, uniform branch
-            f32x4 v = acc[0][nt] * fw[nt >> 3];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                if (w == wave) continue;
-                const u32x2 o = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(
-                    lds0 + (unsigned)(2 * w) * kSlotA + (unsigned)((nt * 64 + lane) * 8));
-                v[0] += __uint_as_float(o[0] << 16) * fw[w];
-                v[1] += __uint_as_float(o[0] & 0xFFFF0000u) * fw[w];
-                v[2] += __uint_as_float(o[1] << 16) * fw[w];
-                v[3] += __uint_as_float(o[1] & 0xFFFF0000u) * fw[w];
-            }
-            v *= inv;
-            const int d = 16 * nt + 4 * g;
-            if (nsplit == 1) {
-                const u32x2 ob = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                *(u32x2*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = ob;
-            } else {
-                *(f32x4*)(p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d) = v;
-            }
-        }
-        if (wave == 0 && g == 0) {
-            const float lse = lt > 0.f ? (mall + __log2f(lt)) * kLn2 : -INFINITY;
-            if (nsplit == 1) p.lse[(size_t)b * p.rows_total + grow] = lse;
-            else p.part_lse[(size_t)slot * p.rows_total + grow] = lse;
-        }
+        for (int ks = 0; ks < 18; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, lds_load16(qa + 64 * ks));
     }
+    wg_barrier();
+    if (wave == 3 && K > 1) issue(1);
+    const int row = blockIdx.y * 16 + c16;
+    const int iq = row / p.h_q;
+    const int lim = min(tok_end, p.causal ? L - (p.s_q - 1 - iq) : L);
+
+    // per-lane LDS offsets: K rows 16 hh + c16 at byte 8 g; V^T source row T(g, c16 / 2) at byte 8 (c16 % 2)
+    const unsigned k_off0 = f8_row(c16) + 8u * (unsigned)g;
+    const unsigned k_off1 = f8_row(16 + c16) + 8u * (unsigned)g;
+    const unsigned v_off = f8_row(f8_token(g, c16 >> 1)) + 8u * (unsigned)(c16 & 1);
+    for (int k = 0; k < K; ++k) {
+        if (k + 1 < K) MLA_WAIT_VM(19); else MLA_WAIT_VM(0);
+        const unsigned sb = slot0 + (unsigned)(k & 1) * kSlotA;
+        const int tok0 = tok_begin + 32 * (wave + 4 * k);
+
+        // the V^T operands and the row scales up front; K rows streamed through
+        // QK^T (four k-steps ahead); the slot is refilled once QK^T has read it
+        u32x2 vr[32];
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) {
+            const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(uintptr_t)(sb + v_off + 16u * dt));
+            vr[dt] = u32x2{(unsigned)t[0], (unsigned)t[1]};
+        }
+        const f32x4 sc0 = *(const lds_f32x4*)(uintptr_t)(sb + 16u * kF8Scale + 16u * g);
+        const f32x4 sc1 = *(const lds_f32x4*)(uintptr_t)(sb + 16u * kF8Scale + 64u + 16u * g);
+
+        // S^T = K Q^T for the two 16-token halves (k-step kk: half kk / 18, step kk % 18)
+        auto kread = [&](int kk) {
+            const unsigned off = (kk < 18 ? k_off0 : k_off1) + 32u * (unsigned)(kk % 18);
+            return *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(sb + off);
+        };
+        f32x4 s[2];
+        {
+            u32x2 kr[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) kr[kk] = kread(kk);
+            f32x4 e[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kk = 0; kk < 36; ++kk) {
+                const int hh = kk / 18, ks = kk % 18;
+                e[2 * hh + (ks & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kr[kk & 3]), qf[ks],
+                                                                            e[2 * hh + (ks & 1)], 0, 0, 0);
+                if (kk + 4 < 36) kr[kk & 3] = kread(kk + 4);
+            }
+            s[0] = e[0] + e[1];
+            s[1] = e[2] + e[3];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (k + 2 < K) issue(k + 2);
+
+        // row scales, mask, online softmax
+        float sv[8], scu[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float sc = e < 4 ? sc0[e] : sc1[e - 4];
+            const int t = tok0 + f8_token(g, e);
+            const bool vis = t < lim;
+            sv[e] = vis ? s[e >> 2][e & 3] * sc * p.scale_log2 : -INFINITY;
+            scu[e] = vis ? sc : 0.f;                           // scales of rows past the end may be anything
+        }
+        float tmax = sv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
+        tmax = xor32_max(xor16_max(tmax));
+        const bool need = tmax > mrun + kLazyTau;
+        if (wave_any(need)) {
+            const float mnew = need ? tmax : mrun;
+            const float alpha = need ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.f;
+            lrun *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < 32; ++nt) acc[nt] *= alpha;
+            mrun = mnew;
+        }
+        const float muse = mrun == -INFINITY ? 0.f : mrun;
+        float pv[8], psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(sv[e] - muse);
+            psum += pe;
+            pv[e] = pe * scu[e];
+        }
+        lrun += xor32_sum(xor16_sum(psum));
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
+
+        // O^T += V^T (P scale)^T, 32 tokens per matrix op
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt)
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(vr[nt]), pb, acc[nt], 0, 0, 0);
+    }
+
+    stream_merge_store(p, acc, mrun, lrun, lds0, slot0, wave, lane, b, slot, nsplit);
+}
+
+hipError_t launch_decode_fp8(const DecodeParams& p, int num_units, int head_groups, hipStream_t stream)
+{
+    dim3 grid(num_units, head_groups);
+    hipLaunchKernelGGL(decode_stream_fp8_kernel, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- split combine

@@ -188,6 +188,32 @@ def algorithmic_counts(seqlens, s_q: int, h_q: int, causal: bool,
     return nbytes, flops
 
 
+
+def fp8_counts(seqlens, s_q: int, h_q: int, causal: bool, d_qk: int = D_QK, d_v: int = D_V, page: int = PAGE):
+    """Algorithmic (bytes, flops) of a decode over the FP8 cache: as algorithmic_counts,
+    but each cached row is d_qk one-byte codes plus its 4-byte float32 scale."""
+    L = np.asarray(seqlens, dtype=np.int64)
+    B = L.shape[0]
+    nb = (L + page - 1) // page
+    nbytes = int(L.sum()) * (d_qk + 4) + B * s_q * h_q * (2 * d_qk + 2 * d_v + 4) + 4 * int(nb.sum()) + 4 * B
+    flops = int(visible_tokens(L, s_q, causal).sum()) * h_q * 2 * (d_qk + d_v)
+    return nbytes, flops
+
+
+def rows_in_token_order(inp: DecodeInputs) -> np.ndarray:
+    """uint16 [B, max_L, d_qk]: sequence b's cached rows in token order, right-aligned
+    (row i holds token L_b - max_L + i; rows before token 0 are zero)."""
+    L = inp.cache_seqlens.astype(np.int64)
+    B = L.shape[0]
+    T = int(L.max()) if B else 0
+    page = inp.kcache.shape[1]
+    rows = np.zeros((B, T, inp.kcache.shape[2]), dtype=np.uint16)
+    for b in range(B):
+        t = np.arange(int(L[b]))
+        rows[b, T - int(L[b]):] = inp.kcache[inp.block_table[b, t // page], t % page]
+    return rows
+
+
 # ---------------------------------------------------------------- cache append
 
 APPEND_SEED = 11
@@ -221,12 +247,14 @@ def make_append(batch: int = 64, s_new: int = 512, seed: int = APPEND_SEED) -> A
     return AppendInputs(kcache=kcache, block_table=table, cache_seqlens=lens, new_rows=new_rows)
 
 
-def append_bytes(inp: AppendInputs) -> int:
-    """Algorithmic HBM bytes of one append: every new row read once and written
-    once, plus the block-table entries and lengths the kernel reads."""
+def append_bytes(inp: AppendInputs, fp8: bool = False) -> int:
+    """Algorithmic HBM bytes of one append: every new row read once (bf16) and written
+    once (bf16, or for the FP8 cache its codes and its 4-byte scale), plus the
+    block-table entries and lengths the kernel reads."""
     B, s_new, width = inp.new_rows.shape
     rows = int(np.minimum(inp.cache_seqlens, s_new).sum())
-    return 2 * rows * width * 2 + 4 * rows + 4 * B
+    written = width + 4 if fp8 else 2 * width
+    return rows * (2 * width + written) + 4 * rows + 4 * B
 
 
 # ---------------------------------------------------------------- sparse decode
