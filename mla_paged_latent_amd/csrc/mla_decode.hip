@@ -53,18 +53,23 @@ hipError_t launch_wide(const DecodeParams& p, dim3 grid, hipStream_t stream);   
 constexpr int kLdsRow = 1168;            // LDS row stride: 72 data chunks + 1 pad chunk of 16 B
 constexpr int kRowSlots = 73;
 
-// Copy rows [0, 16 or 32) of a block run starting at gbase (valid of them real)
-// into an LDS slot; copies first, first+step, ... < ninstr of 1 KB each.
+// Copy the 16 rows of a run starting at gbase (wave-uniform; the first `valid`
+// rows real) into an LDS slot of 1168-byte rows: copy i (first, first + step,
+// ... < ninstr) fills slot chunks [64 i, 64 i + 64), chunk position q holding
+// chunk q mod 73 of row q / 73; the pad chunk and rows >= valid repeat a real
+// chunk. Every copy is issued from the scalar base plus a 32-bit lane offset,
+// and q / 73 = (q * 898) >> 16 holds exactly for every q < 3649 (slots have
+// 1216 positions), so the per-copy address work is a few full-rate 24-bit ops.
 __device__ __forceinline__ void copy_rows(const unsigned char* gbase, int valid, unsigned slot, int first,
                                           int step, int ninstr, int lane)
 {
     for (int i = first; i < ninstr; i += step) {
         const int q = i * 64 + lane;
-        int r = q / kRowSlots;
-        int c = q - r * kRowSlots;
+        int r = (int)(__umul24((unsigned)q, 898u) >> 16);
+        int c = q - kRowSlots * r;
         r = r < valid ? r : 0;
         c = c < kChunks ? c : 0;
-        dma16(gbase + r * kRowBytes + c * 16, slot + (unsigned)i * 1024u);
+        dma16s(gbase, (unsigned)(r * kRowBytes + c * 16), slot + (unsigned)i * 1024u);
     }
 }
 
@@ -441,22 +446,25 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
         const unsigned char* sbase = (const unsigned char*)(p.kscale + row0);
         const int valid = min(32, tok_end - tok);
         const unsigned dst = slot0 + (unsigned)(k & 1) * kSlotA;
+        // Branch-free lane map: position pos holds chunk c of row r, where
+        // pp = pos minus the pad chunk before row 16, r = pp / 37 (exact as
+        // (pp * 1772) >> 16 for pp < 2367), c = pp mod 37; pad chunks and rows
+        // >= valid read the run's first chunk, the last copy also the scales.
+#pragma unroll
         for (int i = 0; i < kDmaA; ++i) {
             const int pos = i * 64 + lane;
-            const unsigned char* src = gbase;                  // pad chunks: any in-bounds bytes
-            if (pos < kF8Scale) {
-                const int hb = pos >= 16 * kF8Chunks;
-                const int pp = hb ? pos - kF8Row16 : pos;
-                if (pp >= 0) {
-                    const int r = pp / kF8Chunks;
-                    const int c = pp - r * kF8Chunks;
-                    const int rr = 16 * hb + r;
-                    if (c < 36) src = gbase + (size_t)(rr < valid ? rr : 0) * kDqk + 16 * c;
-                }
-            } else if (pos < kF8Scale + 8) {
-                src = sbase + 16 * (pos - kF8Scale);
+            const int pp = pos - (pos >= kF8Row16 ? 1 : 0);
+            int r = (int)(__umul24((unsigned)pp, 1772u) >> 16);
+            const int c = pp - kF8Chunks * r;
+            const bool data = pos != kF8Row16 - 1 && c < 36 && r < 32;
+            r = r < valid ? r : 0;
+            const unsigned off = data ? (unsigned)(r * kDqk + 16 * c) : 0u;
+            if (i == kDmaA - 1) {
+                const bool scl = pos >= kF8Scale && pos < kF8Scale + 8;
+                dma16(scl ? sbase + 16 * (pos - kF8Scale) : gbase + off, dst + (unsigned)i * 1024u);
+            } else {
+                dma16s(gbase, off, dst + (unsigned)i * 1024u);
             }
-            dma16(src, dst + (unsigned)i * 1024u);
         }
     };
 

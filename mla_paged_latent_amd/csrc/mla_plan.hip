@@ -14,7 +14,11 @@
 
 namespace mla {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 1024;       // largest workgroup; small batches launch 256 threads
+
+// Threads of the planner for a batch: one workgroup either way; a small batch
+// finishes sooner with fewer waves to synchronise, a large one needs them all.
+inline int plan_threads(int batch) { return batch <= 1024 ? 256 : kPlanThreads; }
 
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ int wave_inclusive_scan(int x)
@@ -28,15 +32,16 @@ __device__ __forceinline__ int wave_inclusive_scan(int x)
     return x;
 }
 
-// Inclusive prefix sum of a[0..n) in LDS by one workgroup of kPlanThreads:
+// Inclusive prefix sum of a[0..n) in LDS by one workgroup (blockDim.x threads):
 // every thread sums a contiguous chunk, the chunk sums are scanned within each
 // wave and across the waves' totals (carry[], one int per wave), then every
 // thread rewrites its chunk. Two workgroup barriers.
 __device__ void block_inclusive_scan(int* a, int n, int* carry)
 {
     const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
     const int wave = tid >> 6;
-    const int per = (n + kPlanThreads - 1) / kPlanThreads;
+    const int per = (n + nthr - 1) / nthr;
     const int lo = tid * per;
     const int hi = min(lo + per, n);
     int local = 0;
@@ -75,20 +80,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     int* NS = P + (batch + 1);           // [batch + 1]
     int* carry = NS + (batch + 1);       // [kPlanThreads / 64]
     const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
 
     if (plan_by_sequence(rows_wg)) {
         // P = prefix sums of the block counts
-        for (int b = tid; b < batch; b += kPlanThreads) P[b + 1] = blocks_of(seqlens[b]);
+        for (int b = tid; b < batch; b += nthr) P[b + 1] = blocks_of(seqlens[b]);
         if (tid == 0) P[0] = 0;
         __syncthreads();
         block_inclusive_scan(P + 1, batch, carry);
         const int W = plan_width(P[batch], num_units - batch);
-        for (int b = tid; b < batch; b += kPlanThreads) NS[b + 1] = ceil_div(P[b + 1] - P[b], W);
+        for (int b = tid; b < batch; b += nthr) NS[b + 1] = ceil_div(P[b + 1] - P[b], W);
         if (tid == 0) NS[0] = 0;
         __syncthreads();
         block_inclusive_scan(NS + 1, batch, carry);
-        for (int b = tid; b <= batch; b += kPlanThreads) splits[b] = NS[b];
-        for (int u = tid; u < num_units; u += kPlanThreads) {
+        for (int b = tid; b <= batch; b += nthr) splits[b] = NS[b];
+        for (int u = tid; u < num_units; u += nthr) {
             int32_t* m = meta + (size_t)u * kMetaInts;
             int b = plan_owner(NS, batch, u);
             if (b >= batch) { write_meta(m, batch, 0, batch, 0, 0, 0, 0, 0); continue; }
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     }
 
     const int kappa = kSegmentCost;
-    for (int b = tid; b < batch; b += kPlanThreads) {
+    for (int b = tid; b < batch; b += nthr) {
         int nb = blocks_of(seqlens[b]);
         P[b + 1] = nb > 0 ? nb + kappa : 0;
     }
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     block_inclusive_scan(P + 1, batch, carry);
 
     const int W = plan_width(P[batch], num_units);
-    for (int b = tid; b < batch; b += kPlanThreads) {
+    for (int b = tid; b < batch; b += nthr) {
         int cost = P[b + 1] - P[b];
         int nb = cost > 0 ? cost - kappa : 0;
         NS[b + 1] = plan_splits(P[b], nb, kappa, W);
@@ -118,9 +124,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (tid == 0) NS[0] = 0;
     __syncthreads();
     block_inclusive_scan(NS + 1, batch, carry);
-    for (int b = tid; b <= batch; b += kPlanThreads) splits[b] = NS[b];
+    for (int b = tid; b <= batch; b += nthr) splits[b] = NS[b];
 
-    for (int u = tid; u < num_units; u += kPlanThreads) {
+    for (int u = tid; u < num_units; u += nthr) {
         int b0, j0, b1, j1;
         plan_locate(P, batch, kappa, u * W, &b0, &j0);
         plan_locate(P, batch, kappa, (u + 1) * W, &b1, &j1);
@@ -185,7 +191,7 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_u
                                            (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, stream, seqlens, batch, rows_wg,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(plan_threads(batch)), lds, stream, seqlens, batch, rows_wg,
                        num_units, meta, splits);
     return hipGetLastError();
 }
