@@ -233,17 +233,26 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     auto issue = [&](int k) {
         const int tok = tok_begin + 16 * (wave + 4 * k);
         if constexpr (SPARSE) {
+            // lanes 0-15 fetch the cache rows of the sub-tile's 16 tokens (padding
+            // and tokens past the list: the fallback row); copy i spans slot rows
+            // r0 = 64 i / 73 and r0 + 1, whose bases are formed in scalar registers
             const unsigned dst = slot0 + (unsigned)(k & 1) * kSlotA;
+            int rid = -1;
+            if (lane < 16 && tok + lane < tok_end)
+                rid = *(const __attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)(tok - tok_begin + lane));
+            rid = rid >= 0 ? rid : fallback;
+            const unsigned char* kc = (const unsigned char*)p.kcache;
+#pragma unroll 1
             for (int i = 0; i < kDmaA; ++i) {
                 const int q = i * 64 + lane;
-                const int r = q / kRowSlots;
-                int c = q - r * kRowSlots;
+                const int r = (int)(__umul24((unsigned)q, 898u) >> 16);
+                int c = q - kRowSlots * r;
                 c = c < kChunks ? c : 0;
-                int rowid = tok + r < tok_end
-                                ? *(const __attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)(tok - tok_begin + r))
-                                : -1;
-                rowid = rowid >= 0 ? rowid : fallback;
-                dma16((const unsigned char*)p.kcache + (size_t)rowid * kRowBytes + c * 16, dst + (unsigned)i * 1024u);
+                const int r0 = (i * 64) / kRowSlots;
+                const int r1 = r0 + 1 < 16 ? r0 + 1 : 0;             // slot positions past row 15: any real row
+                const unsigned char* base0 = kc + (size_t)__builtin_amdgcn_readlane(rid, r0) * kRowBytes;
+                const unsigned char* base1 = kc + (size_t)__builtin_amdgcn_readlane(rid, r1) * kRowBytes;
+                dma16((r == r0 ? base0 : base1) + c * 16, dst + (unsigned)i * 1024u);
             }
             return;
         }
