@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
 # Per-source extra flags. The wide decode kernel uses the VGPR form of the
 # matrix ops, so its output accumulators can be rescaled in place.
 FILE_FLAGS = {
+    # matrix-op accumulators in VGPRs: the online-softmax rescale multiplies them in
+    # place instead of the loop copying them between AGPRs and VGPRs every step
+    "mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "mla_decode_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
