@@ -39,29 +39,52 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
 MALL_BYTES = 256 * 2 ** 20
-DECODE_SRCS = [os.path.join(ROOT, "mla_paged_latent_amd", "csrc", f)
-               for f in ("mla_decode.hip", "mla_decode_wide.hip", "mla_device.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+CSRC = os.path.join(ROOT, "mla_paged_latent_amd", "csrc")
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_decode_wide.hip", "mla_device.h", "mla_common.h")]
+APPEND_SRCS = [os.path.join(CSRC, f) for f in ("mla_append.hip", "mla_common.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_digest() -> str:
+def traffic_key(op: str, workload: str) -> str:
+    """Name of a benchmark case in profiles/traffic.json."""
+    if op == "decode":
+        return workload
+    if op == "fp8":
+        return "fp8_" + workload
+    return op
+
+
+def traffic_kernel(key: str) -> str:
+    """The dominant kernel of a case (a substring of its name in rocprofv3 output)."""
+    if key in ("compute_bound", "mixed"):
+        return "decode_wide_kernel"
+    if key.startswith("fp8_"):
+        return "decode_stream_fp8_kernel"
+    if key == "sparse":
+        return "decode_stream_kernel<1, true>"
+    if key in ("append", "append_fp8"):
+        return key + "_kernel"
+    return "decode_stream_kernel<1, false>"
+
+
+def kernel_source_digest(key: str = "memory_bound") -> str:
     h = hashlib.sha256()
-    for path in DECODE_SRCS:
+    for path in (APPEND_SRCS if key.startswith("append") else DECODE_SRCS):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
-    were taken on the current decode kernel source; else None."""
+def measured_traffic(key: str):
+    """HBM bytes per launch of the case's dominant kernel from committed rocprofv3
+    counter runs, if they were taken on the current source of that kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = doc.get(workload)
-    if not ent or ent.get("kernel_source_sha") != kernel_source_digest():
+    ent = doc.get(key)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_digest(key):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -103,11 +126,12 @@ def _counter_means(csv_dir, counter, name_part):
 
 
 def pmc_summary(args):
-    """Turn FETCH_SIZE / WRITE_SIZE counter runs of the decode kernel, and the same counters
-    over a plain device copy of known size, into HBM bytes per decode launch; stored in
-    profiles/decode_traffic.json under the workload's name."""
+    """Turn FETCH_SIZE / WRITE_SIZE counter runs of a case's dominant kernel, and the same
+    counters over a plain device copy of known size, into HBM bytes per launch; stored in
+    profiles/traffic.json under the case's name (traffic_key)."""
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.pmc_summary
-    kname = "decode_wide_kernel" if args.workload in ("compute_bound", "mixed") else "decode_stream_kernel"
+    key = traffic_key(args.op, args.workload)
+    kname = traffic_kernel(key)
     copy_bytes = args.copy_bytes
     cf, _ = _counter_means(cfetch_dir, "FETCH_SIZE", "copy")
     cw, _ = _counter_means(cwrite_dir, "WRITE_SIZE", "copy")
@@ -123,18 +147,18 @@ def pmc_summary(args):
         "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
         "factor_fetch": round(f_fetch, 4), "factor_write": round(f_write, 4),
         "hbm_bytes_per_launch": int(kf * 1024.0 * f_fetch + kw * 1024.0 * f_write),
-        "kernel_source_sha": kernel_source_digest(),
+        "kernel_source_sha": kernel_source_digest(key),
     }
     try:
         with open(TRAFFIC_FILE) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         doc = {}
-    doc[args.workload] = ent
+    doc[key] = ent
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps({args.workload: ent}))
+    print(json.dumps({key: ent}))
     return 0
 
 
@@ -206,8 +230,8 @@ def bench_append(args, torch, mla, dev):
                    "batch": int(B), "s_new": int(s_new), "replicas": R},
         "alg_bytes_per_step": nbytes,
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_ms_avg": round(ms, 6)},
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.op), "kernel_ms_avg": round(ms, 6)},
     }
     if not args.no_cpu_baseline:
         from oracle import append as oracle_append
@@ -294,8 +318,8 @@ def bench_sparse(args, torch, mla, dev):
                    "batch": B, "s_q": s_q, "h_q": h_q, "topk": topk, "replicas": R, "num_units": units},
         "tflops": round(tf, 3), "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
         "roofline": {"bound": "hbm", "kernel": "sparse decode step (plan + decode + combine)", "achieved": round(gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_ms_avg": round(ms, 6)},
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("sparse"), "kernel_ms_avg": round(ms, 6)},
     }
     if not args.no_cpu_baseline:
         import oracle as orc
@@ -388,8 +412,8 @@ def bench_fp8(args, torch, mla, dev):
                    "num_units": units},
         "tflops": round(tf, 3), "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
         "roofline": {"bound": "hbm", "kernel": "fp8 decode step (plan + decode + combine)", "achieved": round(gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_ms_avg": round(ms, 6)},
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("fp8_" + args.workload), "kernel_ms_avg": round(ms, 6)},
     }
     if not args.no_cpu_baseline:
         import oracle as orc
@@ -427,8 +451,8 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter calibration) and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="no GPU: write the workload's HBM bytes per decode launch to profiles/decode_traffic.json "
-                         "from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv outputs")
+                    help="no GPU: write the HBM bytes per launch of the dominant kernel of --op/--workload to "
+                         "profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv outputs")
     ap.add_argument("--copy-bytes", type=int, default=256 * 2 ** 20, help="size of the calibration copy")
     ap.add_argument("--op", default="decode", choices=["decode", "append", "append_fp8", "sparse", "fp8"],
                     help="decode: the hot path (default); append / append_fp8: the cache-append kernel alone "
@@ -556,7 +580,7 @@ def main(argv=None):
     tflops = flops / (ms_step * 1e-3) / 1e12
     k_gbs = nbytes / (kern_ms * 1e-3) / 1e9
     k_tf = flops / (kern_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(traffic_key("decode", args.workload))
 
     result = {
         "metric": "MLA decode TFLOPS + HBM GB/s (fraction of MI355X peak), paged bf16",
