@@ -228,9 +228,10 @@ int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks,
  * The attention is that of mla_decode_fwd over the decoded values (queries
  * stay bf16); rows no query may read may hold anything, NaN included.
  *
- * mla_fp8_plan_sizes / mla_get_metadata_fp8: the plan for this decode (its
- *   kernel handles 16 query rows per workgroup for every s_q*h_q), same
- *   arguments and outputs as mla_plan_sizes / mla_get_metadata.
+ * mla_fp8_plan_sizes / mla_get_metadata_fp8: the plan for this decode; the
+ *   FP8 decode uses the geometry of the bf16 one (64 query rows per
+ *   workgroup when s_q*h_q is a multiple of 64, else 16), so these return
+ *   exactly what mla_plan_sizes / mla_get_metadata return.
  * mla_decode_fp8_fwd: as mla_decode_fwd with kcache replaced by (kcodes,
  *   kscale); both 16-byte aligned.
  * mla_append_kv_fp8: as mla_append_kv, but each new bf16 row is quantized

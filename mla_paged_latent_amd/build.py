@@ -33,6 +33,7 @@ FILE_FLAGS = {
     # place instead of the loop copying them between AGPRs and VGPRs every step
     "mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "mla_decode_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "mla_decode_wide_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

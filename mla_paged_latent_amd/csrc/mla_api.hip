@@ -13,7 +13,7 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_u
 hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_decode_sparse(const DecodeParams& p, int num_units, int head_groups, hipStream_t stream);
-hipError_t launch_decode_fp8(const DecodeParams& p, int num_units, int head_groups, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream);
 }  // namespace mla
 
 namespace {
@@ -383,45 +383,22 @@ int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks, co
 
 // ---------------------------------------------------------------- FP8 cache decode
 //
-// The FP8 cache is decoded by the 16-row streaming kernel for every s_q*h_q,
-// so its plan is always the per-sequence plan.
+// The FP8 cache is decoded with the same geometry and plan as the bf16 cache:
+// 64-row workgroups (the FP8 wide kernel) when s_q * h_q is a multiple of 64,
+// else 16-row workgroups (the FP8 streaming kernel).
 
 extern "C" {
 
 int mla_fp8_plan_sizes(int batch, int s_q, int h_q, int num_cus, int* num_units, size_t* meta_bytes,
                        size_t* splits_bytes, size_t* workspace_bytes)
 {
-    int rc = check_shape(batch, s_q, h_q);
-    if (rc != MLA_OK) return rc;
-    if (num_cus <= 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
-        if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return MLA_ERR_HIP;
-        if (num_cus <= 0) return MLA_ERR_HIP;
-    }
-    const int rows = s_q * h_q;
-    int units = num_cus / (rows / 16);
-    if (units < batch + 1) units = batch + 1;
-    size_t part_o = 0, total = 0;
-    workspace_layout(batch, rows, units, &part_o, &total);
-    if (num_units) *num_units = units;
-    if (meta_bytes) *meta_bytes = (size_t)units * mla::kMetaInts * sizeof(int32_t);
-    if (splits_bytes) *splits_bytes = (size_t)(batch + 1) * sizeof(int32_t);
-    if (workspace_bytes) *workspace_bytes = total;
-    return MLA_OK;
+    return mla_plan_sizes(batch, s_q, h_q, num_cus, num_units, meta_bytes, splits_bytes, workspace_bytes);
 }
 
 int mla_get_metadata_fp8(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_units,
                          int32_t* tile_meta, int32_t* num_splits, void* stream)
 {
-    int rc = check_shape(batch, s_q, h_q);
-    if (rc != MLA_OK) return rc;
-    if (!cache_seqlens || !tile_meta || !num_splits || num_units < batch + 1) return MLA_ERR_INVALID_ARG;
-    if (mla::launch_plan(cache_seqlens, batch, 16, num_units, tile_meta, num_splits, (hipStream_t)stream) !=
-        hipSuccess)
-        return MLA_ERR_HIP;
-    return MLA_OK;
+    return mla_get_metadata(cache_seqlens, batch, s_q, h_q, num_units, tile_meta, num_splits, stream);
 }
 
 int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, int64_t nblocks,
@@ -438,7 +415,8 @@ int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, i
     if (!aligned16(q) || !aligned16(kcodes) || !aligned16(kscale) || !aligned16(out) || !aligned16(workspace) ||
         ((uintptr_t)lse & 3u))
         return MLA_ERR_INVALID_ARG;
-    if (num_units < batch + 1) return MLA_ERR_INVALID_ARG;
+    const Geometry geo = geometry(s_q, h_q);
+    if (check_units(geo, batch, num_units) != MLA_OK) return MLA_ERR_INVALID_ARG;
     const int rows = s_q * h_q;
     size_t part_o = 0, total = 0;
     workspace_layout(batch, rows, num_units, &part_o, &total);
@@ -467,7 +445,7 @@ int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, i
     p.sq_real = 1;
     p.kscale = kscale;
     hipStream_t st = (hipStream_t)stream;
-    if (mla::launch_decode_fp8(p, num_units, rows / 16, st) != hipSuccess) return MLA_ERR_HIP;
+    if (mla::launch_decode_fp8(p, num_units, geo.head_groups, geo.rows_wg, st) != hipSuccess) return MLA_ERR_HIP;
     return run_combine(p, st);
 }
 

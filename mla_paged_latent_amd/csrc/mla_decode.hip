@@ -48,7 +48,8 @@
 
 namespace mla {
 
-hipError_t launch_wide(const DecodeParams& p, dim3 grid, hipStream_t stream);   // mla_decode_wide.hip
+hipError_t launch_wide(const DecodeParams& p, dim3 grid, hipStream_t stream);       // mla_decode_wide.hip
+hipError_t launch_wide_fp8(const DecodeParams& p, dim3 grid, hipStream_t stream);   // mla_decode_wide_fp8.hip
 
 constexpr int kLdsRow = 1168;            // LDS row stride: 72 data chunks + 1 pad chunk of 16 B
 constexpr int kRowSlots = 73;
@@ -395,24 +396,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
 // [16 dt + 8 p, +8) of token T(G, e) and output lane j gets dim 16 dt + j of
 // the 8 tokens T(G, 0..7) -- the A operand of the 16x16x32 product.
 
-constexpr int kF8Chunks = 37;                        // chunks per LDS row: 36 of codes + 1 pad
-constexpr int kF8Row16 = 16 * kF8Chunks + 1;         // chunk position of row 16
-constexpr int kF8Scale = 2 * 16 * kF8Chunks + 1;     // chunk position of the 32 row scales
-
-__device__ __forceinline__ unsigned f8_row(int r) { return 16u * (unsigned)(kF8Chunks * r + (r >> 4)); }
-
 // token (0..31 within the sub-tile) of element e of a lane of group g in the
 // S^T tiles / P^T operand: elements 0-3 are tile 0 rows 4g..4g+3, 4-7 tile 1
 __device__ __forceinline__ int f8_token(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
-
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw)
-{
-    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.f, false);
-    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.f, true);
-    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.f, false);
-    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.f, true);
-    return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-}
 
 __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
 {
@@ -592,10 +578,14 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
     stream_merge_store(p, acc, mrun, lrun, lds0, slot0, wave, lane, b, slot, nsplit);
 }
 
-hipError_t launch_decode_fp8(const DecodeParams& p, int num_units, int head_groups, hipStream_t stream)
+hipError_t launch_decode_fp8(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream)
 {
     dim3 grid(num_units, head_groups);
-    hipLaunchKernelGGL(decode_stream_fp8_kernel, grid, dim3(256), 0, stream, p);
+    switch (rows_wg) {
+    case 16: hipLaunchKernelGGL(decode_stream_fp8_kernel, grid, dim3(256), 0, stream, p); break;
+    case 64: return launch_wide_fp8(p, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -133,6 +133,28 @@ __device__ __forceinline__ s16x4 lds_tr4(unsigned addr)
 
 __device__ __forceinline__ int token_of_row(int a) { return ((a >> 3) << 3) + ((a & 3) << 1) + ((a >> 2) & 1); }
 
+// ---- FP8 cache staging (both FP8 decode kernels). A 32-token slot is 1216
+// chunks of 16 B (19 one-KB copies): rows 0-15 of E4M3 codes at chunk 37 r,
+// rows 16-31 at 37 r + 1 (576 B of codes + one pad chunk per row; the extra
+// chunk keeps rows r and r + 16 in different banks), then the 32 row scales
+// at chunk 1185.
+constexpr int kF8Chunks = 37;                        // chunks per LDS row: 36 of codes + 1 pad
+constexpr int kF8Row16 = 16 * kF8Chunks + 1;         // chunk position of row 16
+constexpr int kF8Scale = 2 * 16 * kF8Chunks + 1;     // chunk position of the 32 row scales
+constexpr int kF8SlotB = 19 * 1024;                  // one 32-token slot
+
+__device__ __forceinline__ unsigned f8_row(int r) { return 16u * (unsigned)(kF8Chunks * r + (r >> 4)); }
+
+// Eight E4M3 codes -> eight bf16 values, exactly (every E4M3 value is a bf16 value).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 raw)
+{
+    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.f, false);
+    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.f, true);
+    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.f, false);
+    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.f, true);
+    return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
 __device__ __forceinline__ unsigned short bf16_rne(float f)
 {
     unsigned u = __float_as_uint(f);

@@ -80,6 +80,35 @@ def test_fp8_edge_shapes(lens, s_q, h_q):
     assert_parity(out, lse, ro, rl, "fp8 %s" % (lens,))
 
 
+WIDE = [([5, 70, 1, 0, 129, 64, 3], 1, 64, True), ([1, 2, 200], 4, 16, True), ([700, 33], 2, 32, True),
+        ([64, 2048], 1, 128, False), ([0, 0, 65], 1, 64, True), ([3000, 17, 400, 1], 2, 64, True)]
+
+
+@pytest.mark.parametrize("lens,s_q,h_q,causal", WIDE)
+def test_fp8_wide_shapes(lens, s_q, h_q, causal):
+    """s_q * h_q a multiple of 64: the 64-row kernel; units span several short sequences,
+    lengths below s_q, empty sequences, non-causal."""
+    _say("fp8 wide lens=%s s_q=%d h_q=%d causal=%d" % (lens, s_q, h_q, causal))
+    inp = cases.small_batch(lens, s_q=s_q, h_q=h_q, seed=7 * sum(lens) + h_q, causal=causal)
+    codes, scales = fp8.quantize_rows(clean_rows(inp))
+    bad = np.all(inp.kcache == wl.BF16_NAN, axis=-1)
+    codes[bad] = 0x7F
+    scales[bad] = np.nan
+    out, lse = run(inp, codes, scales)
+    ro, rl = ref(inp, codes, scales)
+    assert_parity(out, lse, ro, rl, "fp8 wide %s" % (lens,))
+
+
+@pytest.mark.parametrize("units", [3, 7, 300])
+def test_fp8_wide_plan_extremes(units):
+    _say("fp8 wide units=%d" % units)
+    inp = cases.small_batch([900, 64, 2000, 5, 130], s_q=1, h_q=64, seed=units + 1)
+    codes, scales = fp8.quantize_rows(clean_rows(inp))
+    out, lse = run(inp, codes, scales, num_units=units)
+    ro, rl = ref(inp, codes, scales)
+    assert_parity(out, lse, ro, rl, "wide units %d" % units)
+
+
 @pytest.mark.parametrize("units", [17, 40, 900])
 def test_fp8_plan_extremes(units):
     _say("fp8 units=%d" % units)
@@ -128,6 +157,20 @@ def test_fp8_append_then_decode():
     torch.cuda.synchronize()
     ro, rl = ref(inp, rc, rs)
     assert_parity(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, "append+decode")
+
+
+def test_fp8_mixed_sampled_rows():
+    """The mixed workload (s_q=2, h_q=128, causal, lengths 256-16384) on the FP8 cache; sampled sequences."""
+    _say("fp8 mixed sampled")
+    inp = wl.make_workload("mixed", poison=False)
+    codes, scales = fp8.quantize_rows(inp.kcache)
+    out, lse = run(inp, codes, scales)
+    lens = inp.cache_seqlens
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5})
+    for b in pick:
+        sub = wl.subset(inp, [b])
+        ro, rl = ref(sub, codes, scales)
+        assert_parity(out[[b]], lse[[b]], ro, rl, "mixed row %d" % b)
 
 
 def test_fp8_compute_bound_sampled_rows():
