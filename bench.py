@@ -40,7 +40,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
 MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "mla_paged_latent_amd", "csrc")
-DECODE_SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_decode_wide.hip", "mla_device.h", "mla_common.h")]
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_decode_wide.hip", "mla_decode_wide_fp8.hip",
+                                                "mla_device.h", "mla_common.h")]
 APPEND_SRCS = [os.path.join(CSRC, f) for f in ("mla_append.hip", "mla_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -58,6 +59,8 @@ def traffic_kernel(key: str) -> str:
     """The dominant kernel of a case (a substring of its name in rocprofv3 output)."""
     if key in ("compute_bound", "mixed"):
         return "decode_wide_kernel"
+    if key in ("fp8_compute_bound", "fp8_mixed"):
+        return "decode_wide_fp8_kernel"
     if key.startswith("fp8_"):
         return "decode_stream_fp8_kernel"
     if key == "sparse":
