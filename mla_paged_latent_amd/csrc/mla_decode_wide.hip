@@ -26,8 +26,8 @@ namespace mla {
 //    row group), reading the four P^T tiles back from LDS.
 // S^T = K Q^T puts the scores in the layout of the P^T operand of
 // O^T = V^T P^T, so P is packed to bf16 where it is computed. Block halves
-// hold rows of 1152 B with chunk c of row r at position c ^ (r % 8), which with
-// the token permutation keeps b128 and transpose reads conflict free.
+// hold rows of 1152 B with their chunks permuted (swz below), which with the
+// token permutation keeps b128 and transpose reads conflict free.
 
 constexpr int kHalfB = 32 * kRowBytes;          // 36,864 B: 32 token rows, 36 copies of 1 KB
 constexpr int kBlockB = 2 * kHalfB;             // 73,728 B: one cache block
@@ -66,8 +66,17 @@ __device__ __forceinline__ Segment next_segment(const DecodeParams& p, int b, in
     return none;
 }
 
-// LDS byte offset of chunk c of row r in a swizzled block half.
-__device__ __forceinline__ unsigned swz(int r, int c) { return (unsigned)(r * kRowBytes + ((c ^ (r & 7)) << 4)); }
+// Chunk permutation of row r of a block half: chunk c is stored at position
+// c ^ f(r) with f(r) = ((r << 1) ^ (r >> 2)) mod 16, chunks 64-71 by the low
+// three bits of f only (so they stay in 64-71); the map is its own inverse.
+// The LDS serves a 16-byte read 16 lanes per cycle from 16 groups of four
+// banks, and row r starts in group 8r mod 16: with this f the 16 rows of a
+// K fragment read (any chunk) and the 4 rows x 4 chunks of a V^T transpose
+// read each fall in 16 different groups. (Rows are unpadded: two blocks and
+// the inboxes fill the LDS.)
+__device__ __forceinline__ int swz_f(int r) { return ((r << 1) ^ (r >> 2)) & 15; }
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c < 64 ? (c ^ swz_f(r)) : (c ^ (swz_f(r) & 7)); }
+__device__ __forceinline__ unsigned swz(int r, int c) { return (unsigned)(r * kRowBytes + (swz_chunk(r, c) << 4)); }
 
 __device__ __forceinline__ float lds_f(unsigned addr) { return *(const lds_f32*)(uintptr_t)addr; }
 
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     for (int k = 0; k < 9; ++k) {
         const int q = (wave + 4 * k) * 64 + lane;
         const int r = q / kChunks;
-        goff[k] = (unsigned)(r * kRowBytes + (((q - r * kChunks) ^ (r & 7)) << 4));
+        goff[k] = swz(r, q - r * kChunks);
     }
     int n_issued = 0;
     // The next block of the copy cursor goes to LDS block (n_issued % 2):
@@ -158,27 +167,28 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     };
     issue();
 
-    // QK^T A operand (K rows): token row tokA; for k-step ks = 4 j + m its chunk
-    // is 36 kh + 2 ks + h, stored at ((36 kh + h + 2 m) ^ (tokA % 8)) + 8 j
+    // QK^T A operand (K rows): token row tokA; for k-step ks its chunk is
+    // 36 kh + 2 ks + h (64 or more only for kh = 1, ks >= 14)
     const int tokA = token_of_row(r32);
-    unsigned k_off[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-        k_off[m] = (unsigned)(tokA * kRowBytes + (((36 * kh + h + 2 * m) ^ (tokA & 7)) << 4));
+    const unsigned k_row = (unsigned)(tokA * kRowBytes);
+    const int k_f = swz_f(tokA);
+    auto k_off = [&](int ks) {
+        const int c = 36 * kh + 2 * ks + h;
+        return k_row + (unsigned)(((kh && ks >= 14) ? (c ^ (k_f & 7)) : (c ^ k_f)) << 4);
+    };
     // PV A operand (transposed V): source row token_of_row(16 kp + 8 half + 4h + i16/4),
-    // dims 128 wave + 32 dt + 16 dh + 4 (i16 % 4), i.e. chunk 16 wave + 4 dt + 2 dh + (i16 % 4)/2;
-    // dt = 2 (dt/2) + par, and the dt/2 part is a plain +128 B
-    unsigned v_off[2][2][2];
+    // dims 128 wave + 32 dt + 16 dh + 4 (i16 % 4), i.e. chunk 16 wave + 4 dt + 2 dh + (i16 % 4)/2 (< 64)
+    unsigned v_row[2][2];
+    int v_f[2][2];
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int par = 0; par < 2; ++par) {
-                const int r = token_of_row(16 * kp + 8 * half + 4 * h + (i16 >> 2));
-                const int ch = 16 * wave + 4 * par + 2 * dh + ((i16 & 3) >> 1);
-                v_off[kp][half][par] = swz(r, ch) + 8u * (unsigned)(i16 & 1);
-            }
+        for (int half = 0; half < 2; ++half) {
+            const int r = token_of_row(16 * kp + 8 * half + 4 * h + (i16 >> 2));
+            v_row[kp][half] = (unsigned)(r * kRowBytes) + 8u * (unsigned)(i16 & 1);
+            v_f[kp][half] = swz_f(r);
+        }
+    const int v_c = 16 * wave + 2 * dh + ((i16 & 3) >> 1);
 
     int n = 0;                                              // block being computed
     while (cs.b < p.batch) {
@@ -232,14 +242,14 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
                 const unsigned dst = copy_dst();
                 s16x8 kv[4];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kv[ks] = lds_load16(sb + k_off[ks & 3] + 128u * (unsigned)(ks >> 2));
+                for (int ks = 0; ks < 4; ++ks) kv[ks] = lds_load16(sb + k_off(ks));
 #pragma unroll
                 for (int ks = 0; ks < 18; ++ks) {
                     __builtin_amdgcn_sched_barrier(0);
                     const bf16x8 a = __builtin_bit_cast(bf16x8, kv[ks & 3]);
                     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][ks], s0, 0, 0, 0);
                     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][ks], s1, 0, 0, 0);
-                    if (ks + 4 < 18) kv[ks & 3] = lds_load16(sb + k_off[(ks + 4) & 3] + 128u * (unsigned)((ks + 4) >> 2));
+                    if (ks + 4 < 18) kv[ks & 3] = lds_load16(sb + k_off(ks + 4));
                     if constexpr (decltype(with_copy)::value) copy_full(gbase, dst, ks);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -338,9 +348,9 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
                 s16x4 va[2][2];
                 auto load_v = [&](int k, s16x4* d) {
                     const int dt = k >> 1, kp = k & 1;
-                    const unsigned off = 128u * (unsigned)(dt >> 1);
-                    d[0] = lds_tr4(sb + v_off[kp][0][dt & 1] + off);
-                    d[1] = lds_tr4(sb + v_off[kp][1][dt & 1] + off);
+                    const int c = v_c + 4 * dt;
+                    d[0] = lds_tr4(sb + v_row[kp][0] + (unsigned)((c ^ v_f[kp][0]) << 4));
+                    d[1] = lds_tr4(sb + v_row[kp][1] + (unsigned)((c ^ v_f[kp][1]) << 4));
                 };
 #pragma unroll
                 for (int k = 0; k < 2; ++k) load_v(k, va[k]);
