@@ -35,9 +35,11 @@
 //    j element e is element j%4 of what source lane 4e + j/4 read, so source
 //    lanes read 4 dims of 4 token rows and every output lane ends with one dim
 //    of 4 tokens -- the MFMA A operand;
-//  * the MFMA row <-> token map is permuted, token(a) = 8(a/8) + 2(a%4) + (a/4)%2,
-//    so that 8 consecutive A rows hit 8 different 16-byte bank groups and the 4
-//    rows a transpose read combines hit 4 different 32-byte bank groups;
+//  * the MFMA row <-> token map is permuted so that fragment reads and
+//    transpose reads fall in distinct LDS bank groups: rows 0-7 of the 16-row
+//    tiles are the even tokens and rows 8-15 the odd ones (stream_token); the
+//    32-row tiles of the wide kernel use token(a) = 8(a/8) + 2(a%4) + (a/4)%2
+//    with a chunk permutation of their own;
 //  * scores are scaled into the exp2 domain; the running max is raised (and O
 //    rescaled) only when a score exceeds it by more than 2^8, so P <= 256;
 //  * rows past the end of a sequence are loaded from the block's first valid
@@ -53,6 +55,15 @@ hipError_t launch_wide_fp8(const DecodeParams& p, dim3 grid, hipStream_t stream)
 
 constexpr int kLdsRow = 1168;            // LDS row stride: 72 data chunks + 1 pad chunk of 16 B
 constexpr int kRowSlots = 73;
+
+// Token (0..15) of row a of the 16-row MFMA tiles of the streaming kernel:
+// rows 0-7 are the even tokens, rows 8-15 the odd ones. The LDS serves a
+// read from 16 groups of four banks and slot row t starts in group 9t mod 16
+// (1168 = 73 x 16 B): a K fragment read (16 rows, one chunk) hits 16 groups for
+// any order, and the first (second) 32 lanes of a V^T transpose read (8 rows,
+// two adjacent chunks) hit 16 groups because their rows are the even (odd)
+// tokens, whose groups 9t mod 16 are all even (odd).
+__device__ __forceinline__ int stream_token(int a) { return 2 * (a & 7) + (a >> 3); }
 
 // Copy the 16 rows of a run starting at gbase (wave-uniform; the first `valid`
 // rows real) into an LDS slot of 1168-byte rows: copy i (first, first + step,
@@ -298,8 +309,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
         lim[rt] = SPARSE ? tok_end : min(tok_end, p.causal ? L - (p.s_q - 1 - iq) : L);
     }
 
-    const unsigned a_off = (unsigned)(token_of_row(c16) * kLdsRow + g * 16);
-    const unsigned v_off = (unsigned)(token_of_row(4 * g + (c16 >> 2)) * kLdsRow + 8 * (c16 & 3));
+    const unsigned a_off = (unsigned)(stream_token(c16) * kLdsRow + g * 16);
+    const unsigned v_off = (unsigned)(stream_token(4 * g + (c16 >> 2)) * kLdsRow + 8 * (c16 & 3));
     for (int k = 0; k < K; ++k) {
         if (k + 1 < K) MLA_WAIT_VM(19); else MLA_WAIT_VM(0);
         const unsigned sb = slot0 + (unsigned)(k & 1) * kSlotA;
@@ -330,14 +341,14 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
             s[rt] = e0 + e1;
         }
 
-        // scale, mask, online softmax; s[rt][i] is token tok0 + token_of_row(4g + i)
+        // scale, mask, online softmax; s[rt][i] is token tok0 + stream_token(4g + i)
         s16x4 pb[NR];
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
             float tmax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = tok0 + token_of_row(4 * g + i);
+                const int t = tok0 + stream_token(4 * g + i);
                 bool vis = t < lim[rt];
                 if constexpr (SPARSE)
                     vis = vis && *(const __attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)(t - tok_begin)) >= 0;
