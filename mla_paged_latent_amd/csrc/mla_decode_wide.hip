@@ -37,47 +37,6 @@ constexpr int kLdsB = 2 * kBlockB + 4 * kXB;    // 163,840 B
 // (all 4 KB), afterwards its owner's row maxima, P^T tile and row sums.
 constexpr unsigned kXMax = 0, kXP = 128, kXSum = 2176;
 
-// The run of sequence b inside a unit: tokens [tb, te) of a sequence of L tokens.
-struct Segment {
-    int b, tb, te, L;
-};
-
-__device__ __forceinline__ Segment unit_segment(const DecodeParams& p, int b, int b0, int j0, int b1, int j1)
-{
-    Segment s;
-    s.b = b;
-    s.L = cload(p.seqlens + b);
-    const int nb = blocks_of(s.L);
-    s.tb = (b == b0 ? j0 : 0) * kPage;
-    const int je = (b == b1) ? j1 : nb;
-    s.te = min(je * kPage, s.L);
-    return s;
-}
-
-// First non-empty segment of the unit at or after sequence b (b = batch when none).
-__device__ __forceinline__ Segment next_segment(const DecodeParams& p, int b, int b0, int j0, int b1, int j1)
-{
-    for (; b <= b1 && b < p.batch; ++b) {
-        Segment s = unit_segment(p, b, b0, j0, b1, j1);
-        if (s.tb < s.te) return s;
-    }
-    Segment none;
-    none.b = p.batch; none.tb = 0; none.te = 0; none.L = 0;
-    return none;
-}
-
-// Chunk permutation of row r of a block half: chunk c is stored at position
-// c ^ f(r) with f(r) = ((r << 1) ^ (r >> 2)) mod 16, chunks 64-71 by the low
-// three bits of f only (so they stay in 64-71); the map is its own inverse.
-// The LDS serves a 16-byte read 16 lanes per cycle from 16 groups of four
-// banks, and row r starts in group 8r mod 16: with this f the 16 rows of a
-// K fragment read (any chunk) and the 4 rows x 4 chunks of a V^T transpose
-// read each fall in 16 different groups. (Rows are unpadded: two blocks and
-// the inboxes fill the LDS.)
-__device__ __forceinline__ int swz_f(int r) { return ((r << 1) ^ (r >> 2)) & 15; }
-__device__ __forceinline__ int swz_chunk(int r, int c) { return c < 64 ? (c ^ swz_f(r)) : (c ^ (swz_f(r) & 7)); }
-__device__ __forceinline__ unsigned swz(int r, int c) { return (unsigned)(r * kRowBytes + (swz_chunk(r, c) << 4)); }
-
 __device__ __forceinline__ float lds_f(unsigned addr) { return *(const lds_f32*)(uintptr_t)addr; }
 
 __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)

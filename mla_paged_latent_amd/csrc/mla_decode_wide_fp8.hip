@@ -35,33 +35,6 @@ constexpr int kLdsF = 2 * kF8BlockB + 4 * kXBf + 4 * kCopyMapB;    // 104,448 B
 constexpr unsigned kXMaxF = 0, kXPF = 128, kXSumF = 2176;
 constexpr unsigned kScaleLane = 0x80000000u;        // copy-map flag: the lane brings row scales
 
-struct SegmentF {
-    int b, tb, te, L;
-};
-
-__device__ __forceinline__ SegmentF unit_segment_f(const DecodeParams& p, int b, int b0, int j0, int b1, int j1)
-{
-    SegmentF s;
-    s.b = b;
-    s.L = cload(p.seqlens + b);
-    const int nb = blocks_of(s.L);
-    s.tb = (b == b0 ? j0 : 0) * kPage;
-    const int je = (b == b1) ? j1 : nb;
-    s.te = min(je * kPage, s.L);
-    return s;
-}
-
-__device__ __forceinline__ SegmentF next_segment_f(const DecodeParams& p, int b, int b0, int j0, int b1, int j1)
-{
-    for (; b <= b1 && b < p.batch; ++b) {
-        SegmentF s = unit_segment_f(p, b, b0, j0, b1, j1);
-        if (s.tb < s.te) return s;
-    }
-    SegmentF none;
-    none.b = p.batch; none.tb = 0; none.te = 0; none.L = 0;
-    return none;
-}
-
 __device__ __forceinline__ float lds_ff(unsigned addr) { return *(const lds_f32*)(uintptr_t)addr; }
 
 // Copy c (0..37) of a block: slot c / 19, copy c % 19 of that slot. Lane map
@@ -130,11 +103,11 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
     const unsigned xin = lds0 + 2 * kF8BlockB;              // inbox of wave 0
     const unsigned xmine = xin + (unsigned)wave * kXBf;
 
-    SegmentF is = next_segment_f(p, b0, b0, j0, b1, j1);   // copy cursor
+    Segment is = next_segment(p, b0, b0, j0, b1, j1);   // copy cursor
     if (is.b >= p.batch) return;
     int itok = is.tb;
     int ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
-    SegmentF cs = is;                                       // compute cursor
+    Segment cs = is;                                       // compute cursor
 
     // this wave copies c = wave + 4k of each block (10 copies for waves 0-1, 9 for 2-3);
     // the lane offsets of a whole block are computed once and kept in LDS
@@ -154,7 +127,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
         ++n_issued;
         itok += kPage;
         if (itok >= is.te) {
-            is = next_segment_f(p, is.b + 1, b0, j0, b1, j1);
+            is = next_segment(p, is.b + 1, b0, j0, b1, j1);
             itok = is.tb;
         }
         if (is.b < p.batch) ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
@@ -397,7 +370,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
                 else p.part_lse[(size_t)slot * p.rows_total + row] = lse;
             }
         }
-        cs = next_segment_f(p, cs.b + 1, b0, j0, b1, j1);
+        cs = next_segment(p, cs.b + 1, b0, j0, b1, j1);
     }
 }
 

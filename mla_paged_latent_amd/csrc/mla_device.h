@@ -169,4 +169,47 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b)
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+// ---------------------------------------------------------------- units of the cost-line plan
+
+// The run of sequence b inside a unit: tokens [tb, te) of a sequence of L tokens.
+struct Segment {
+    int b, tb, te, L;
+};
+
+__device__ __forceinline__ Segment unit_segment(const DecodeParams& p, int b, int b0, int j0, int b1, int j1)
+{
+    Segment s;
+    s.b = b;
+    s.L = cload(p.seqlens + b);
+    const int nb = blocks_of(s.L);
+    s.tb = (b == b0 ? j0 : 0) * kPage;
+    const int je = (b == b1) ? j1 : nb;
+    s.te = min(je * kPage, s.L);
+    return s;
+}
+
+// First non-empty segment of the unit at or after sequence b (b = batch when none).
+__device__ __forceinline__ Segment next_segment(const DecodeParams& p, int b, int b0, int j0, int b1, int j1)
+{
+    for (; b <= b1 && b < p.batch; ++b) {
+        Segment s = unit_segment(p, b, b0, j0, b1, j1);
+        if (s.tb < s.te) return s;
+    }
+    Segment none;
+    none.b = p.batch; none.tb = 0; none.te = 0; none.L = 0;
+    return none;
+}
+
+// Chunk permutation of a row r of a 32-row block half in LDS (64- and 128-row
+// kernels; rows are unpadded): chunk c is stored at position c ^ f(r) with
+// f(r) = ((r << 1) ^ (r >> 2)) mod 16, chunks 64-71 by the low three bits of
+// f only (so they stay in 64-71); the map is its own inverse. The LDS serves
+// a 16-byte read 16 lanes per cycle from 16 groups of four banks, and row r
+// starts in group 8r mod 16: with this f the 16 rows of a K fragment read
+// (any chunk) and the 4 rows x 4 chunks of a V^T transpose read each fall in
+// 16 different groups.
+__device__ __forceinline__ int swz_f(int r) { return ((r << 1) ^ (r >> 2)) & 15; }
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c < 64 ? (c ^ swz_f(r)) : (c ^ (swz_f(r) & 7)); }
+__device__ __forceinline__ unsigned swz(int r, int c) { return (unsigned)(r * kRowBytes + (swz_chunk(r, c) << 4)); }
+
 }  // namespace mla

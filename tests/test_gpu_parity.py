@@ -97,6 +97,8 @@ SHAPES = [
     ([70, 190], 2, 32),                      # 64 rows, causal
     ([5, 129, 700], 1, 128),                 # two head groups of 64
     ([3, 66, 500], 4, 32),                   # 128 rows, causal over 4 new tokens
+    ([31, 32, 33, 95, 96, 97, 161], 1, 128),  # block halves cut at every place
+    ([1, 40, 3000, 64], 2, 64),              # 128 rows, causal, one long and three short
     ([2, 65, 300], 2, 128),                  # 256 rows: four head groups
     ([7, 64, 0, 900], 3, 64),                # 192 rows, an empty sequence
     ([10, 140], 3, 16),                      # 48 rows: three head groups of 16
@@ -123,8 +125,8 @@ def test_non_causal_multi_token():
     assert_parity(out, lse, ref_out, ref_lse, "non-causal")
 
 
-@pytest.mark.parametrize("h_q,units", [(16, 6), (16, 7), (16, 40), (16, 2000), (128, 1), (128, 2), (128, 7),
-                                        (128, 300)])
+@pytest.mark.parametrize("h_q,units", [(16, 6), (16, 7), (16, 40), (16, 2000), (64, 3), (64, 300), (128, 1),
+                                        (128, 2), (128, 7), (128, 300)])
 def test_plan_extremes_give_the_same_answer(h_q, units):
     inp = cases.small_batch([1, 640, 65, 2000, 128], s_q=1, h_q=h_q, seed=17)
     _say("plan with %d units, h_q=%d" % (units, h_q))
