@@ -70,6 +70,65 @@ __device__ __host__ inline void write_meta(int32_t* m, int b0, int j0, int b1, i
     m[5] = len; m[6] = first_slot; m[7] = nsplit;
 }
 
+// Per-sequence plan: first block of split k of a sequence of n blocks cut
+// into ns runs (split_begin), in 32-bit arithmetic when k * n fits.
+__device__ __forceinline__ int split_begin_dev(int n, int ns, int k)
+{
+    const long long kn = (long long)k * n;
+    return kn < 0x7FFFFFFF ? (int)kn / ns : (int)(kn / ns);
+}
+
+// Batches of at most 64 sequences: every wave builds the prefix sums of its
+// own from one sequence per lane (wave scans, a private copy in LDS), so the
+// workgroup needs no barrier; threads then fill the units' rows as below.
+__device__ void plan_small(const int32_t* __restrict__ seqlens, int batch, int rows_wg, int num_units,
+                           int32_t* __restrict__ meta, int32_t* __restrict__ splits, int* smem)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    int* P = smem + (tid >> 6) * 2 * 65;                    // [65]: this wave's copy
+    int* NS = P + 65;                                       // [65]
+    const int len = lane < batch ? seqlens[lane] : 0;
+    const int nb = blocks_of(len);
+    const bool by_seq = plan_by_sequence(rows_wg);
+    const int kappa = by_seq ? 0 : kSegmentCost;
+    const int cost = nb > 0 ? nb + kappa : 0;
+    const int pin = wave_inclusive_scan(cost);
+    const int total = __shfl(pin, 63, 64);
+    const int W = by_seq ? plan_width(total, num_units - batch) : plan_width(total, num_units);
+    const int ns = lane < batch ? (by_seq ? ceil_div(nb, W) : plan_splits(pin - cost, nb, kappa, W)) : 0;
+    const int nsin = wave_inclusive_scan(ns);
+    P[lane + 1] = pin;
+    NS[lane + 1] = nsin;
+    if (lane == 0) { P[0] = 0; NS[0] = 0; }
+    // a wave's LDS accesses complete in order: once its stores are issued, its
+    // lanes read each other's entries (the asm keeps the compiler from moving
+    // loads above them)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (tid < 64)
+        for (int i = lane; i <= batch; i += 64) splits[i] = NS[i];
+    for (int u = tid; u < num_units; u += blockDim.x) {
+        int32_t* m = meta + (size_t)u * kMetaInts;
+        if (by_seq) {
+            const int b = plan_owner(NS, batch, u);
+            if (b >= batch) { write_meta(m, batch, 0, batch, 0, 0, 0, 0, 0); continue; }
+            const int n = P[b + 1] - P[b];
+            const int nsb = NS[b + 1] - NS[b];
+            const int k = u - NS[b];
+            write_meta(m, b, split_begin_dev(n, nsb, k), b, split_begin_dev(n, nsb, k + 1), k, seqlens[b], NS[b] + k,
+                       nsb);
+        } else {
+            int b0, j0, b1, j1;
+            plan_locate(P, batch, kappa, u * W, &b0, &j0);
+            plan_locate(P, batch, kappa, (u + 1) * W, &b1, &j1);
+            const bool any = b0 < batch && (b0 != b1 || j0 != j1);
+            const int split = any ? u - (P[b0] + kappa) / W : 0;
+            write_meta(m, b0, j0, b1, j1, split, any ? seqlens[b0] : 0, any ? NS[b0] + split : 0,
+                       any ? NS[b0 + 1] - NS[b0] : 0);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seqlens, int batch,
                                                              int rows_wg, int num_units,
                                                              int32_t* __restrict__ meta,
@@ -82,6 +141,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
 
+    if (batch <= 64) {
+        plan_small(seqlens, batch, rows_wg, num_units, meta, splits, plan_smem);
+        return;
+    }
     if (plan_by_sequence(rows_wg)) {
         // P = prefix sums of the block counts
         for (int b = tid; b < batch; b += nthr) P[b + 1] = blocks_of(seqlens[b]);
@@ -186,6 +249,7 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_u
                        int32_t* splits, hipStream_t stream)
 {
     size_t lds = sizeof(int) * (2 * (size_t)(batch + 1) + kPlanThreads / 64);
+    if (batch <= 64) lds = sizeof(int) * 2 * 65 * (plan_threads(batch) / 64);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds);

@@ -192,6 +192,25 @@ def test_device_plan_large_batch(h_q, units):
     assert np.array_equal(dmeta.cpu().numpy(), hmeta) and np.array_equal(dsplits.cpu().numpy(), hsplits)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_device_plan_small_batches(seed):
+    """Batches of at most 64 sequences take the planner's per-wave path; its rows equal the host planner's
+    for both plan shapes, empty sequences and unit counts from the least accepted to many more than blocks."""
+    rng = np.random.default_rng(500 + seed)
+    for trial in range(8):
+        B = 64 if trial == 0 else int(rng.integers(1, 65))
+        lens = rng.integers(0, 9000, B).astype(np.int32)
+        lens[rng.random(B) < 0.15] = 0
+        s_q, h_q = [(1, 16), (2, 16), (1, 64), (1, 128), (3, 16), (2, 64)][(seed + trial) % 6]
+        by_sequence = (s_q * h_q) % 64 != 0
+        units = int(rng.choice([1, 2, 7, 64, 256, 999])) + (B if by_sequence else 0)
+        _say("small plan B=%d s_q=%d h_q=%d units=%d" % (B, s_q, h_q, units))
+        dmeta, dsplits = mla.mla_get_metadata(torch.from_numpy(lens).cuda(), h_q, s_q, num_units=units)
+        hmeta, hsplits = mla.mla_get_metadata_host(lens, h_q, s_q, units)
+        assert np.array_equal(dmeta.cpu().numpy(), hmeta), (B, s_q, h_q, units)
+        assert np.array_equal(dsplits.cpu().numpy(), hsplits), (B, s_q, h_q, units)
+
+
 # ------------------------------------------------------------- graph capture
 
 @pytest.mark.parametrize("lens,s_q,h_q", [([700, 65, 3000, 1], 1, 16), ([300, 2000, 64], 2, 128)])
