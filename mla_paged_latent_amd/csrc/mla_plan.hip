@@ -79,15 +79,17 @@ __device__ __forceinline__ int split_begin_dev(int n, int ns, int k)
 }
 
 // Batches of at most 64 sequences: every wave builds the prefix sums of its
-// own from one sequence per lane (wave scans, a private copy in LDS), so the
-// workgroup needs no barrier; threads then fill the units' rows as below.
+// own from one sequence per lane (wave scans, a private copy in LDS with the
+// lengths), so the workgroup needs no barrier and the units' rows need no
+// second global load; threads then fill the rows as below.
 __device__ void plan_small(const int32_t* __restrict__ seqlens, int batch, int rows_wg, int num_units,
                            int32_t* __restrict__ meta, int32_t* __restrict__ splits, int* smem)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    int* P = smem + (tid >> 6) * 2 * 65;                    // [65]: this wave's copy
+    int* P = smem + (tid >> 6) * 3 * 65;                    // [65]: this wave's copy
     int* NS = P + 65;                                       // [65]
+    int* LEN = NS + 65;                                     // [64]: cache_seqlens
     const int len = lane < batch ? seqlens[lane] : 0;
     const int nb = blocks_of(len);
     const bool by_seq = plan_by_sequence(rows_wg);
@@ -100,6 +102,7 @@ __device__ void plan_small(const int32_t* __restrict__ seqlens, int batch, int r
     const int nsin = wave_inclusive_scan(ns);
     P[lane + 1] = pin;
     NS[lane + 1] = nsin;
+    LEN[lane] = len;
     if (lane == 0) { P[0] = 0; NS[0] = 0; }
     // a wave's LDS accesses complete in order: once its stores are issued, its
     // lanes read each other's entries (the asm keeps the compiler from moving
@@ -115,15 +118,14 @@ __device__ void plan_small(const int32_t* __restrict__ seqlens, int batch, int r
             const int n = P[b + 1] - P[b];
             const int nsb = NS[b + 1] - NS[b];
             const int k = u - NS[b];
-            write_meta(m, b, split_begin_dev(n, nsb, k), b, split_begin_dev(n, nsb, k + 1), k, seqlens[b], NS[b] + k,
-                       nsb);
+            write_meta(m, b, split_begin_dev(n, nsb, k), b, split_begin_dev(n, nsb, k + 1), k, LEN[b], NS[b] + k, nsb);
         } else {
             int b0, j0, b1, j1;
             plan_locate(P, batch, kappa, u * W, &b0, &j0);
             plan_locate(P, batch, kappa, (u + 1) * W, &b1, &j1);
             const bool any = b0 < batch && (b0 != b1 || j0 != j1);
             const int split = any ? u - (P[b0] + kappa) / W : 0;
-            write_meta(m, b0, j0, b1, j1, split, any ? seqlens[b0] : 0, any ? NS[b0] + split : 0,
+            write_meta(m, b0, j0, b1, j1, split, any ? LEN[b0] : 0, any ? NS[b0] + split : 0,
                        any ? NS[b0 + 1] - NS[b0] : 0);
         }
     }
@@ -249,7 +251,7 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int rows_wg, int num_u
                        int32_t* splits, hipStream_t stream)
 {
     size_t lds = sizeof(int) * (2 * (size_t)(batch + 1) + kPlanThreads / 64);
-    if (batch <= 64) lds = sizeof(int) * 2 * 65 * (plan_threads(batch) / 64);
+    if (batch <= 64) lds = sizeof(int) * 3 * 65 * (plan_threads(batch) / 64);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds);
