@@ -90,81 +90,72 @@ constexpr int kDmaA = 19;
 constexpr int kLdsA = 8 * kSlotA;        // two slots per wave: 155,648 B
 
 // Merge the four waves' (m, l, O) of a 16-row streaming workgroup and write
-// the result. Wave w owns output tiles nt in [8w, 8w + 8) (dims [128w,
-// 128w + 128)) and keeps them in registers. As soon as it is done with its
-// slots it posts its other 24 tiles (unscaled, bf16) and its running max/sum
-// per row into its own slot area; one workgroup barrier later every wave folds
-// in the others' tiles. acc[nt] element i is dim 16 nt + 4 (lane / 16) + i of
-// row lane % 16 of the workgroup's rows.
-__device__ __forceinline__ void stream_merge_store(const DecodeParams& p, const f32x4* acc, float mrun_, float lrun_,
+// the result. As soon as a wave is done with its slots it posts its 32 tiles
+// (unscaled, bf16) and its running max/sum per row into its own slot area; one
+// workgroup barrier later wave w folds the four waves' tiles nt in [8w, 8w + 8)
+// (dims [128w, 128w + 128)) and writes them. Register indices are static and
+// only LDS and global addresses depend on the wave, so the code is executed by
+// every wave alike (it runs once per launch, from a cold instruction cache).
+// acc[nt] element i is dim 16 nt + 4 (lane / 16) + i of row lane % 16 of the
+// workgroup's rows.
+__device__ __forceinline__ void stream_merge_store(const DecodeParams& p, const f32x4* acc, float mrun, float lrun,
                                                    unsigned lds0, unsigned slot0, int wave, int lane, int b, int slot,
                                                    int nsplit)
 {
     constexpr int R = 16;
     const int g = lane >> 4;
     const int c16 = lane & 15;
-    f32x4 accl[32];
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt) accl[nt] = acc[nt];
-    float mrun[1] = {mrun_}, lrun[1] = {lrun_};
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");       // this wave's slot reads are done
-    {
-        const unsigned mine = slot0;
-        if (g == 0) {
-            *(lds_f32*)(uintptr_t)(mine + 16384u + 4u * c16) = mrun[0];
-            *(lds_f32*)(uintptr_t)(mine + 16384u + 64u + 4u * c16) = lrun[0];
-        }
+    if (g == 0) {
+        *(lds_f32*)(uintptr_t)(slot0 + 16384u + 4u * c16) = mrun;
+        *(lds_f32*)(uintptr_t)(slot0 + 16384u + 64u + 4u * c16) = lrun;
+    }
 #pragma unroll
-        for (int nt = 0; nt < 32; ++nt) {
-            if ((nt >> 3) == wave) continue;
-            const u32x2 v = {pack_bf16x2(accl[nt][0], accl[nt][1]), pack_bf16x2(accl[nt][2], accl[nt][3])};
-            *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(mine + (unsigned)((nt * 64 + lane) * 8)) = v;
-        }
+    for (int nt = 0; nt < 32; ++nt) {
+        const u32x2 v = {pack_bf16x2(acc[nt][0], acc[nt][1]), pack_bf16x2(acc[nt][2], acc[nt][3])};
+        *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(slot0 + (unsigned)((nt * 64 + lane) * 8)) = v;
     }
     wg_barrier();
-    {
-        float mw[4], mall = -INFINITY;
+    float mw[4], mall = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        mw[w] = *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 4u * c16);
+        mall = fmaxf(mall, mw[w]);
+    }
+    float fw[4], lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        fw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mall);
+        lt += *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 64u + 4u * c16) * fw[w];
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int grow = blockIdx.y * R + c16;
+    const unsigned tile0 = (unsigned)((8 * wave * 64 + lane) * 8);     // this wave's first tile in a posting
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            mw[w] = *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 4u * c16);
-            mall = fmaxf(mall, mw[w]);
+            const u32x2 o = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(
+                lds0 + (unsigned)(2 * w) * kSlotA + tile0 + 512u * t);
+            v[0] += __uint_as_float(o[0] << 16) * fw[w];
+            v[1] += __uint_as_float(o[0] & 0xFFFF0000u) * fw[w];
+            v[2] += __uint_as_float(o[1] << 16) * fw[w];
+            v[3] += __uint_as_float(o[1] & 0xFFFF0000u) * fw[w];
         }
-        float fw[4], lt = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            fw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mall);
-            lt += *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 64u + 4u * c16) * fw[w];
+        v *= inv;
+        const int d = 16 * (8 * wave + t) + 4 * g;
+        if (nsplit == 1) {
+            const u32x2 ob = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *(u32x2*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = ob;
+        } else {
+            *(f32x4*)(p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d) = v;
         }
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int grow = blockIdx.y * R + c16;
-#pragma unroll
-        for (int nt = 0; nt < 32; ++nt) {
-            if ((nt >> 3) != wave) continue;                  // static tile index, uniform branch
-            f32x4 v = accl[nt] * fw[nt >> 3];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                if (w == wave) continue;
-                const u32x2 o = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(
-                    lds0 + (unsigned)(2 * w) * kSlotA + (unsigned)((nt * 64 + lane) * 8));
-                v[0] += __uint_as_float(o[0] << 16) * fw[w];
-                v[1] += __uint_as_float(o[0] & 0xFFFF0000u) * fw[w];
-                v[2] += __uint_as_float(o[1] << 16) * fw[w];
-                v[3] += __uint_as_float(o[1] & 0xFFFF0000u) * fw[w];
-            }
-            v *= inv;
-            const int d = 16 * nt + 4 * g;
-            if (nsplit == 1) {
-                const u32x2 ob = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                *(u32x2*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = ob;
-            } else {
-                *(f32x4*)(p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d) = v;
-            }
-        }
-        if (wave == 0 && g == 0) {
-            const float lse = lt > 0.f ? (mall + __log2f(lt)) * kLn2 : -INFINITY;
-            if (nsplit == 1) p.lse[(size_t)b * p.rows_total + grow] = lse;
-            else p.part_lse[(size_t)slot * p.rows_total + grow] = lse;
-        }
+    }
+    if (wave == 0 && g == 0) {
+        const float lse = lt > 0.f ? (mall + __log2f(lt)) * kLn2 : -INFINITY;
+        if (nsplit == 1) p.lse[(size_t)b * p.rows_total + grow] = lse;
+        else p.part_lse[(size_t)slot * p.rows_total + grow] = lse;
     }
 }
 
