@@ -129,28 +129,35 @@ __device__ __forceinline__ void stream_merge_store(const DecodeParams& p, const 
         lt += *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 64u + 4u * c16) * fw[w];
     }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float sw[4];                                            // weight of wave w's posting, 1/l folded in
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sw[w] = fw[w] * inv;
     const int grow = blockIdx.y * R + c16;
     const unsigned tile0 = (unsigned)((8 * wave * 64 + lane) * 8);     // this wave's first tile in a posting
+    f32x4 v[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const u32x2 o = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(
                 lds0 + (unsigned)(2 * w) * kSlotA + tile0 + 512u * t);
-            v[0] += __uint_as_float(o[0] << 16) * fw[w];
-            v[1] += __uint_as_float(o[0] & 0xFFFF0000u) * fw[w];
-            v[2] += __uint_as_float(o[1] << 16) * fw[w];
-            v[3] += __uint_as_float(o[1] & 0xFFFF0000u) * fw[w];
+            v[t][0] += __uint_as_float(o[0] << 16) * sw[w];
+            v[t][1] += __uint_as_float(o[0] & 0xFFFF0000u) * sw[w];
+            v[t][2] += __uint_as_float(o[1] << 16) * sw[w];
+            v[t][3] += __uint_as_float(o[1] & 0xFFFF0000u) * sw[w];
         }
-        v *= inv;
-        const int d = 16 * (8 * wave + t) + 4 * g;
-        if (nsplit == 1) {
-            const u32x2 ob = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            *(u32x2*)(p.out + ((size_t)b * p.rows_total + grow) * kDv + d) = ob;
-        } else {
-            *(f32x4*)(p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + d) = v;
-        }
+    }
+    // tile 8 wave + t holds dims 128 wave + 16 t + 4 g .. + 4 of the lane's row
+    if (nsplit == 1) {
+        uint16_t* o = p.out + ((size_t)b * p.rows_total + grow) * kDv + 128 * wave + 4 * g;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            *(u32x2*)(o + 16 * t) = u32x2{pack_bf16x2(v[t][0], v[t][1]), pack_bf16x2(v[t][2], v[t][3])};
+    } else {
+        float* o = p.part_o + ((size_t)slot * p.rows_total + grow) * kDv + 128 * wave + 4 * g;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) *(f32x4*)(o + 16 * t) = v[t];
     }
     if (wave == 0 && g == 0) {
         const float lse = lt > 0.f ? (mall + __log2f(lt)) * kLn2 : -INFINITY;
