@@ -1,22 +1,25 @@
 """Benchmark: MLA decode over a paged bf16 latent cache on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload memory_bound]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixed]
 
 One step is one pass of the whole decode path over one synthetic batch:
 mla_get_metadata (split-KV plan) then mla_decode_fwd (decode kernel + split
 combine). Each step reads a different replica of (kcache, block_table, q), and
 the replicas together exceed twice the 256 MB Infinity Cache, so the cache is
 read from HBM. After W untimed steps, K steps captured in one HIP graph are replayed
-between two events on the launch stream.
-Prints one JSON line.
+between two events on the launch stream. Prints one JSON line.
 
-value = algorithmic bytes per step / step time (GB/s); algorithmic bytes
-count each cached row once plus q, out, lse, the used block-table entries and
-cache_seqlens. tflops = (QK^T + PV MAC flops) / step time. The roofline entry
-is for the decode kernel alone: after the step timing, K decode-kernel launches
-(graphs holding only mla_decode_fwd_splits) run back to back over the replicas
-between two events on the same stream, and achieved = algorithmic bytes (or
-flops) per launch / the average launch time.
+The default workload is mixed (B=128, s_q=2, h_q=128), the largest one-GPU
+configuration; it sits above the ridge of the roofline, so value is TFLOP/s
+(the QK^T + PV MAC flops per step / step time) and gbs beside it the
+algorithmic bytes per step / step time (each cached row counted once, plus q,
+out, lse, the used block-table entries and cache_seqlens). Below the ridge
+(memory_bound, long, tiny) value is GB/s. The plan alone (plan_ms) and the
+decode call alone (decode_fwd_ms) are timed the same way. The roofline entry
+is for the decode kernel alone: K launches (graphs holding only
+mla_decode_fwd_splits) run back to back over the replicas between two events
+on the same stream, and achieved = algorithmic flops (or bytes) per launch / the
+average launch time.
 """
 from __future__ import annotations
 
@@ -92,24 +95,115 @@ def measured_traffic(key: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, nbytes_total, min_seconds=10.0, max_reps=50):
-    """The oracle, as it is, on the host cores: whole batches until min_seconds have passed."""
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def spread_sample(batch: int, k: int):
+    """k sequence indices spread evenly over [0, batch) (so a sample keeps the batch's length mix)."""
+    k = max(1, min(int(k), batch))
+    return sorted(set(int(round(x)) for x in np.linspace(0, batch - 1, k)))
+
+
+def median_rate(seconds, nbytes, flops):
+    """(median seconds, GB/s, TFLOP/s) of repeated passes over a sample of nbytes / flops."""
+    med = float(np.median(np.asarray(seconds, dtype=np.float64)))
+    return med, nbytes / med / 1e9, flops / med / 1e12
+
+
+def cpu_baseline(inp, bound: str, budget_s: float = 20.0, one_thread: bool = False):
+    """The oracle, as it is, on the host cores: a sample of the batch's sequences (spread
+    over the batch) sized so that one pass takes about budget_s / 5 seconds, timed three
+    times; the median pass gives the rates. With one_thread, the same on one thread."""
     import oracle
-    threads = oracle.default_threads()
     oracle.load()
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.decode_inputs(inp, nthreads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or reps >= max_reps:
-            break
-    per = el / reps
-    return {"value": round(nbytes_total / per / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "tflops": round(inp_flops(inp) / per / 1e12, 6),
-            "sample": "%d full passes over the %s batch (B=%d), %.1f s wall, float64 oracle"
-                      % (reps, inp.name, inp.batch, el)}
+    threads = oracle.default_threads()
+
+    def passes(sub, nth, n=3):
+        out = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            oracle.decode_inputs(sub, nthreads=nth)
+            out.append(time.perf_counter() - t0)
+        return out
+
+    def sized_sample(nth, target):
+        # calibrate on one sequence, then grow the sample to about `target` seconds per pass
+        k = 1
+        while True:
+            idx = spread_sample(inp.batch, k)
+            sub = wl.subset(inp, idx)
+            t0 = time.perf_counter()
+            oracle.decode_inputs(sub, nthreads=nth)
+            el = time.perf_counter() - t0
+            if el >= target / 4 or len(idx) == inp.batch:
+                break
+            k = min(inp.batch, max(k + 1, int(k * min(8.0, target / max(el, 1e-4)))))
+        if el < target and len(idx) < inp.batch:
+            idx = spread_sample(inp.batch, min(inp.batch, max(len(idx), int(len(idx) * target / max(el, 1e-4)))))
+        return idx
+
+    def leg(nth, target):
+        idx = sized_sample(nth, target)
+        sub = wl.subset(inp, idx)
+        nb, fl = wl.algorithmic_counts(sub.cache_seqlens, sub.s_q, sub.h_q, sub.causal)
+        secs = passes(sub, nth)
+        med, gbs, tf = median_rate(secs, nb, fl)
+        return idx, secs, med, gbs, tf
+
+    idx, secs, med, gbs, tf = leg(threads, budget_s / 5)
+    res = {"value": round(tf, 6) if bound == "mfma" else round(gbs, 4),
+           "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+           "cores": threads, "kind": "oracle", "gbs": round(gbs, 4), "tflops": round(tf, 6),
+           "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+           "sample": "%d of the %d sequences of the %s batch (evenly spread), float64 oracle on %d threads, "
+                     "median of 3 passes (%s s)" % (len(idx), inp.batch, inp.name, threads,
+                                                   ", ".join("%.2f" % x for x in secs))}
+    if one_thread:
+        idx1, secs1, med1, gbs1, tf1 = leg(1, budget_s / 5)
+        res["one_thread"] = {"gbs": round(gbs1, 4), "tflops": round(tf1, 6),
+                             "sample": "%d of the %d sequences, 1 thread, median of 3 passes (%s s)"
+                                       % (len(idx1), inp.batch, ", ".join("%.2f" % x for x in secs1))}
+    return res
+
+
+def context_ceilings(torch, dev):
+    """Measured ceilings of this GPU, for context beside the spec peaks: a 1 GiB device copy
+    (torch's copy kernel; read + write bytes / time) and an 8192^3 bf16 GEMM (torch.matmul)."""
+    n = 2 ** 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    torch.cuda.synchronize()
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return min(t)
+
+    ms_copy = best(lambda: dst.copy_(src))
+    ms_gemm = best(lambda: a @ b)
+    del src, dst, a, b
+    return {"copy_gbs": round(2 * n / (ms_copy * 1e-3) / 1e9, 1),
+            "gemm_bf16_tflops": round(2 * 8192 ** 3 / (ms_gemm * 1e-3) / 1e12, 1),
+            "how": "best of 5: 1 GiB torch copy (read + write bytes), 8192^3 bf16 torch.matmul"}
 
 
 def _counter_means(csv_dir, counter, name_part):
@@ -451,10 +545,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="memory_bound", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--workload", default="mixed", choices=sorted(wl.WORKLOADS),
+                    help="default: mixed, the largest single-GPU configuration")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 2x the 256 MB cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="about the CPU-baseline leg's wall time")
+    ap.add_argument("--no-context", action="store_true", help="skip the copy / GEMM ceiling measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter calibration) and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -530,6 +626,17 @@ def main(argv=None):
         mla.mla_decode_fwd(q, kc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal,
                            out=out, lse=lse, workspace=ws)
 
+    def plan_only(k):
+        ln = reps[k % R][3]
+        meta, splits = plans[k % R]
+        mla.mla_get_metadata(ln, h_q, s_q, num_units=units, tile_meta=meta, num_splits=splits)
+
+    def decode_fwd(k):
+        kc, q, tab, ln = reps[k % R]
+        meta, splits = plans[k % R]
+        mla.mla_decode_fwd(q, kc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal,
+                           out=out, lse=lse, workspace=ws)
+
     def decode_only(k):
         kc, q, tab, ln = reps[k % R]
         meta, splits = plans[k % R]
@@ -566,16 +673,23 @@ def main(argv=None):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n, host
 
+    def graph_ms(fn):
+        g = capture(fn, args.steps)
+        g.replay()
+        ms, host = timed(g.replay, args.steps)
+        del g
+        return ms, host
+
     steps_graph = capture(step, args.steps)
     if args.warmup:
         capture(step, args.warmup).replay()
     ms_step, host_ms = timed(steps_graph.replay, args.steps)
     del steps_graph
+    # the plan alone and the decode call alone (decode kernel + combine), K launches back to back
+    plan_ms, _ = graph_ms(plan_only)
+    fwd_ms, _ = graph_ms(decode_fwd)
     # the decode kernel alone, K launches back to back over the replicas: the roofline figure
-    dec_graph = capture(decode_only, args.steps)
-    dec_graph.replay()
-    kern_ms, host_kern_ms = timed(dec_graph.replay, args.steps)
-    del dec_graph
+    kern_ms, host_kern_ms = graph_ms(decode_only)
     n_eager = min(args.steps, 50)
 
     def eager():
@@ -583,7 +697,8 @@ def main(argv=None):
             step(k)
     eager_ms, eager_host_ms = timed(eager, n_eager)
 
-    value = nbytes / (ms_step * 1e-3) / 1e9
+    bound = "hbm" if flops / nbytes < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
     tflops = flops / (ms_step * 1e-3) / 1e12
     k_gbs = nbytes / (kern_ms * 1e-3) / 1e9
     k_tf = flops / (kern_ms * 1e-3) / 1e12
@@ -591,8 +706,8 @@ def main(argv=None):
 
     result = {
         "metric": "MLA decode TFLOPS + HBM GB/s (fraction of MI355X peak), paged bf16",
-        "value": round(value, 2),
-        "unit": "GB/s",
+        "value": round(tflops, 3) if bound == "mfma" else round(gbs, 2),
+        "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -606,16 +721,23 @@ def main(argv=None):
                                "scale 1/sqrt(192)" % (args.workload, wl.DESCRIPTIONS[args.workload]),
                    "batch": B, "s_q": s_q, "h_q": h_q, "tokens": int(inp.cache_seqlens.sum()),
                    "replicas": R, "num_units": units},
+        "step": "mla_get_metadata + mla_decode_fwd (plan, decode kernel, split combine); value and "
+                "ms_per_step include the plan",
         "tflops": round(tflops, 3),
-        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "gbs": round(gbs, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+        "plan_ms": round(plan_ms, 6),
+        "decode_fwd_ms": round(fwd_ms, 6),
+        "decode_fwd_tflops": round(flops / (fwd_ms * 1e-3) / 1e12, 3),
+        "decode_fwd_gbs": round(nbytes / (fwd_ms * 1e-3) / 1e9, 2),
         "host_ms_per_step": round(host_ms, 6),
         "eager_ms_per_step": round(eager_ms, 6),
         "eager_host_ms_per_step": round(eager_host_ms, 6),
         "alg_bytes_per_step": nbytes,
         "alg_flops_per_step": flops,
         "roofline": {
-            "bound": "hbm" if flops / nbytes < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma",
+            "bound": bound,
             "kernel": "decode kernel (mla_decode_fwd_splits)",
             "achieved": round(k_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -628,12 +750,16 @@ def main(argv=None):
             "host_ms_per_launch": round(host_kern_ms, 6),
         },
     }
-    if result["roofline"]["bound"] == "mfma":
+    if bound == "mfma":
         r = result["roofline"]
         r.update({"achieved": round(k_tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                  "frac": round(k_tf / BF16_PEAK_TFLOPS, 5), "kernel_gbs": round(k_gbs, 2)})
+                  "frac": round(k_tf / BF16_PEAK_TFLOPS, 5), "kernel_gbs": round(k_gbs, 2),
+                  "kernel_hbm_frac": round(k_gbs / HBM_PEAK_GBS, 4)})
+    if not args.no_context:
+        result["context"] = context_ceilings(torch, dev)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, nbytes, min_seconds=args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(inp, bound, budget_s=args.cpu_seconds,
+                                              one_thread=args.workload in ("tiny", "memory_bound"))
     print(json.dumps(result), flush=True)
     return 0
 

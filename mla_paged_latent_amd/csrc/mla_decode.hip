@@ -18,15 +18,16 @@
 //    in the loop), so each CU keeps up to 8 x 18 KB of cache in flight. The
 //    four waves' partial softmax states are merged once at the end. QK^T on
 //    v_mfma_f32_16x16x32_bf16, PV on v_mfma_f32_16x16x16_bf16.
-//  * Wide kernel (64 query rows): two row groups of 32, each split over two
-//    waves (QK^T by column halves, PV by output-dim halves), share a ring of
-//    four 32-token LDS slots (three in flight while one is used); QK^T and PV
-//    on v_mfma_f32_32x32x16_bf16. A unit may cover several sequences.
+//  * Wide kernel (64 query rows, mla_decode_wide.hip): the workgroup's waves
+//    share two 64-token block buffers in LDS (the block being computed and the
+//    next one in flight); QK^T and PV on v_mfma_f32_32x32x16_bf16. A unit may
+//    cover several sequences.
 //
 // Data path common to both:
 //  * a cache block is 64 contiguous rows of 1152 B; in the streaming kernel an
 //    LDS row is 72 chunks of 16 B plus one pad chunk (stride 1168 B), in the
-//    wide kernel it is unpadded with chunk c of row r stored at c ^ (r % 8);
+//    wide kernel it is unpadded with chunk c of row r stored at c ^ f(r),
+//    f(r) = ((r << 1) ^ (r >> 2)) mod 16 (chunks 64-71 by f's low three bits);
 //  * S^T = K Q^T: K rows are the MFMA A operand (ds_read_b128), Q^T the B
 //    operand held in VGPRs. The S^T accumulator layout (lane = query row,
 //    4 tokens per element group) is exactly the P^T B operand of O^T = V^T P^T,

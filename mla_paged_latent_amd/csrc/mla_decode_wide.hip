@@ -72,8 +72,8 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     Segment cs = is;                                        // compute cursor
 
     // This wave's copies of a block: copy i = wave + 4k of each half (36 per
-    // half); lane l of copy i fills position s of row r (72 r + s = 64 i + l)
-    // of the half with chunk s ^ (r % 8) of that row.
+    // half); lane l of copy i reads chunk c of row r (72 r + c = 64 i + l) of
+    // the half and lands at its permuted position swz(r, c).
     unsigned goff[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) {

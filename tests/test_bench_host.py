@@ -105,3 +105,18 @@ def test_more_than_one_gpu_is_refused():
                        cwd=str(ROOT), timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_spread_sample_keeps_the_ends_and_is_bounded():
+    assert bench.spread_sample(128, 5) == [0, 32, 64, 95, 127]
+    assert bench.spread_sample(16, 40) == list(range(16))
+    assert bench.spread_sample(7, 0) == [0]
+
+
+def test_median_rate_arithmetic():
+    med, gbs, tf = bench.median_rate([3.0, 1.0, 2.0], 4e9, 6e12)
+    assert med == 2.0 and gbs == 2.0 and tf == 3.0
+
+
+def test_cpu_model_is_a_string():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
