@@ -56,6 +56,7 @@ extern "C" {
 #define MLA_D_V 512             /* value width: the first 512 columns of a cached row */
 #define MLA_PAGE_SIZE 64        /* tokens per cache block */
 #define MLA_META_INTS 8         /* int32 entries per work unit in tile_meta */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)  /* device scratch of mla_decode_fwd_noalloc */
 
 typedef enum mla_status {
     MLA_OK = 0,
@@ -177,6 +178,28 @@ int mla_decode_fwd_splits(const void* q, const void* kcache, int64_t nblocks,
 
 int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, int num_units,
                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Arguments, results and checks are those
+ * of mla_decode_fwd; the split partials go to a fixed device array of
+ * MLA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends. The call allocates nothing and calls no
+ * allocating routine; the first call on a device looks the array's address up
+ * once (make that call outside a stream capture).
+ * Limit: the workspace mla_workspace_bytes reports for (batch, s_q, h_q,
+ *   num_units) must fit in MLA_NOALLOC_SCRATCH_BYTES, else
+ *   MLA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (several streams, several host threads) race; serialise them.
+ */
+int mla_decode_fwd_noalloc(const void* q, const void* kcache, int64_t nblocks,
+                           const int32_t* block_table, int max_blocks,
+                           const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                           float softmax_scale, int causal,
+                           const int32_t* tile_meta, const int32_t* num_splits, int num_units,
+                           void* out, float* lse, void* stream);
 
 /*
  * Sparse (top-k index) decode: each new token attends over its own list of

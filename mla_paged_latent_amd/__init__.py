@@ -58,6 +58,8 @@ def load_library(path: Path | str | None = None):
     for name in ("mla_decode_fwd", "mla_decode_fwd_splits"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = dec
+    lib.mla_decode_fwd_noalloc.restype = i32
+    lib.mla_decode_fwd_noalloc.argtypes = dec[:16] + [vp]
     lib.mla_combine_splits.restype = i32
     lib.mla_combine_splits.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.mla_sparse_plan_sizes.restype = i32
@@ -244,6 +246,20 @@ def mla_decode_fwd_splits(q, kcache, block_table, cache_seqlens, softmax_scale: 
                                                  num_splits, causal, out, lse, workspace)
         _check("mla_decode_fwd_splits", load_library().mla_decode_fwd_splits(*args))
     return out, lse, workspace
+
+
+def mla_decode_fwd_noalloc(q, kcache, block_table, cache_seqlens, softmax_scale: float, tile_meta, num_splits,
+                           causal: bool = True, out=None, lse=None):
+    """mla_decode_fwd with the split partials in the library's fixed device scratch
+    (no workspace; the C call allocates nothing). out / lse are allocated here when
+    not given. Returns (out, lse)."""
+    import torch
+    with _on(torch, q.device):
+        dummy = torch.empty((16,), dtype=torch.uint8, device=q.device)
+        args, out, lse, _ = _decode_args(q, kcache, block_table, cache_seqlens, softmax_scale, tile_meta,
+                                         num_splits, causal, out, lse, dummy)
+        _check("mla_decode_fwd_noalloc", load_library().mla_decode_fwd_noalloc(*(args[:16] + (args[18],))))
+    return out, lse
 
 
 def mla_combine_splits(num_splits, s_q: int, h_q: int, num_units: int, out, lse, workspace):

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mla_paged_latent.h"
 #include "mla_common.h"
 
@@ -267,6 +269,72 @@ int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, i
     p.batch = batch;
     p.rows_total = geo.rows_total;
     return run_combine(p, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free decode
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops): the split partials live in one file-scope device
+// array instead of a caller workspace. Each GPU the library runs on holds its
+// own copy of the array until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns on that device (the name
+// itself is a host-side stand-in). Every call on a GPU shares that GPU's
+// array, so calls that overlap in time on one GPU race.
+
+static __device__ __attribute__((aligned(256))) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+int scratch_of_current_device(void** ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return MLA_ERR_HIP;
+        g_scratch[dev] = addr;
+    }
+    *ptr = g_scratch[dev];
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_fwd_noalloc(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table,
+                           int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                           float softmax_scale, int causal, const int32_t* tile_meta, const int32_t* num_splits,
+                           int num_units, void* out, float* lse, void* stream)
+{
+    // every argument and the size this call needs are checked before any HIP
+    // call; a 256-aligned stand-in takes the workspace's place in the checks
+    mla::DecodeParams p;
+    Geometry geo;
+    int rc = setup_decode(q, kcache, nblocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                          softmax_scale, causal, tile_meta, num_splits, num_units, out, lse, (void*)(uintptr_t)256,
+                          MLA_NOALLOC_SCRATCH_BYTES, &p, &geo);
+    if (rc != MLA_OK) return rc;
+    void* ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc != MLA_OK) return rc;
+    size_t part_o = 0, total = 0;
+    workspace_layout(batch, geo.rows_total, num_units, &part_o, &total);
+    p.part_o = (float*)ws;
+    p.part_lse = (float*)((char*)ws + part_o);
+    hipStream_t st = (hipStream_t)stream;
+    if (mla::launch_decode(p, num_units, geo.head_groups, geo.rows_wg, st) != hipSuccess) return MLA_ERR_HIP;
+    return run_combine(p, st);
 }
 
 }  // extern "C"

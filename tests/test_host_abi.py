@@ -217,3 +217,22 @@ def test_per_sequence_plan_needs_a_unit_per_sequence(lib):
         mla.mla_get_metadata_host([10, 20, 30], 16, 1, 3)
     meta, splits = mla.mla_get_metadata_host([10, 20, 30], 16, 1, 4)
     assert splits[-1] == 3
+
+
+def test_noalloc_decode_refuses_more_than_its_scratch_before_any_hip_call(lib):
+    """The allocation-free decode checks its arguments and the workspace the call needs
+    against the fixed scratch (MLA_NOALLOC_SCRATCH_BYTES = 128 MiB) before it touches the
+    GPU: the mixed workload's plan fits, a larger batch or more units does not."""
+    args = _decode_args()
+    ok_units = mla.mla_plan_sizes(128, 2, 128, num_cus=256)["num_units"]
+    assert mla.mla_workspace_bytes(128, 2, 128, ok_units) <= 128 << 20
+    assert mla.mla_workspace_bytes(256, 2, 128, 256) > 128 << 20
+
+    def call(**over):
+        a = _decode_args(**over)
+        return lib.mla_decode_fwd_noalloc(*(a[:16] + [a[18]]))
+    assert call(batch=256, s_q=2, h_q=128, units=256, max_blocks=300) == MLA_ERR_WORKSPACE_TOO_SMALL
+    assert call(batch=16, s_q=1, h_q=16, units=100000) == MLA_ERR_WORKSPACE_TOO_SMALL
+    assert call(q=None) == MLA_ERR_INVALID_ARG
+    assert call(h_q=15) == MLA_ERR_UNSUPPORTED
+    assert call(units=2) == MLA_ERR_INVALID_ARG
