@@ -700,7 +700,12 @@ def main(argv=None):
     bound = "hbm" if flops / nbytes < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     tflops = flops / (ms_step * 1e-3) / 1e12
-    k_gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    # the decode kernel's own algorithmic bytes: out/lse of sequences the plan split are
+    # written by the combine kernel, so they are not credited to it
+    _, host_splits = mla.mla_get_metadata_host(inp.cache_seqlens, h_q, s_q, units)
+    split_rows = int((np.diff(host_splits) > 1).sum()) * s_q * h_q
+    kernel_bytes = nbytes - split_rows * (2 * wl.D_V + 4)
+    k_gbs = kernel_bytes / (kern_ms * 1e-3) / 1e9
     k_tf = flops / (kern_ms * 1e-3) / 1e12
     traffic = measured_traffic(traffic_key("decode", args.workload))
 
@@ -744,6 +749,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(k_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "kernel_alg_bytes": kernel_bytes,
             "kernel_ms_avg": round(kern_ms, 6),
             "kernel_tflops": round(k_tf, 3),
             "kernel_mfma_frac": round(k_tf / BF16_PEAK_TFLOPS, 5),

@@ -92,13 +92,15 @@ constexpr int kLdsA = 8 * kSlotA;        // two slots per wave: 155,648 B
 
 // Merge the four waves' (m, l, O) of a 16-row streaming workgroup and write
 // the result. As soon as a wave is done with its slots it posts its 32 tiles
-// (unscaled, bf16) and its running max/sum per row into its own slot area; one
-// workgroup barrier later wave w folds the four waves' tiles nt in [8w, 8w + 8)
-// (dims [128w, 128w + 128)) and writes them. Register indices are static and
-// only LDS and global addresses depend on the wave, so the code is executed by
-// every wave alike (it runs once per launch, from a cold instruction cache).
-// acc[nt] element i is dim 16 nt + 4 (lane / 16) + i of row lane % 16 of the
-// workgroup's rows.
+// (unscaled fp32, 32 KB) and its running max/sum per row into its own slot
+// area; one workgroup barrier later wave w folds the four waves' tiles nt in
+// [8w, 8w + 8) (dims [128w, 128w + 128)) and writes them. Register indices are
+// static and only LDS and global addresses depend on the wave, so the code is
+// executed by every wave alike (it runs once per launch, from a cold
+// instruction cache). acc[nt] element i is dim 16 nt + 4 (lane / 16) + i of
+// row lane % 16 of the workgroup's rows.
+constexpr unsigned kPostML = 32768;      // a wave's posting: 32 fp32 tiles, then row max and row sum
+
 __device__ __forceinline__ void stream_merge_store(const DecodeParams& p, const f32x4* acc, float mrun, float lrun,
                                                    unsigned lds0, unsigned slot0, int wave, int lane, int b, int slot,
                                                    int nsplit)
@@ -108,46 +110,38 @@ __device__ __forceinline__ void stream_merge_store(const DecodeParams& p, const 
     const int c16 = lane & 15;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");       // this wave's slot reads are done
     if (g == 0) {
-        *(lds_f32*)(uintptr_t)(slot0 + 16384u + 4u * c16) = mrun;
-        *(lds_f32*)(uintptr_t)(slot0 + 16384u + 64u + 4u * c16) = lrun;
+        *(lds_f32*)(uintptr_t)(slot0 + kPostML + 4u * c16) = mrun;
+        *(lds_f32*)(uintptr_t)(slot0 + kPostML + 64u + 4u * c16) = lrun;
     }
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-        const u32x2 v = {pack_bf16x2(acc[nt][0], acc[nt][1]), pack_bf16x2(acc[nt][2], acc[nt][3])};
-        *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(slot0 + (unsigned)((nt * 64 + lane) * 8)) = v;
-    }
+    for (int nt = 0; nt < 32; ++nt)
+        *(lds_f32x4*)(uintptr_t)(slot0 + (unsigned)((nt * 64 + lane) * 16)) = acc[nt];
     wg_barrier();
     float mw[4], mall = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        mw[w] = *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 4u * c16);
+        mw[w] = *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + kPostML + 4u * c16);
         mall = fmaxf(mall, mw[w]);
     }
     float fw[4], lt = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         fw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mall);
-        lt += *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + 16384u + 64u + 4u * c16) * fw[w];
+        lt += *(const lds_f32*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + kPostML + 64u + 4u * c16) * fw[w];
     }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     float sw[4];                                            // weight of wave w's posting, 1/l folded in
 #pragma unroll
     for (int w = 0; w < 4; ++w) sw[w] = fw[w] * inv;
     const int grow = blockIdx.y * R + c16;
-    const unsigned tile0 = (unsigned)((8 * wave * 64 + lane) * 8);     // this wave's first tile in a posting
+    const unsigned tile0 = (unsigned)((8 * wave * 64 + lane) * 16);    // this wave's first tile in a posting
     f32x4 v[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const u32x2 o = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(
-                lds0 + (unsigned)(2 * w) * kSlotA + tile0 + 512u * t);
-            v[t][0] += __uint_as_float(o[0] << 16) * sw[w];
-            v[t][1] += __uint_as_float(o[0] & 0xFFFF0000u) * sw[w];
-            v[t][2] += __uint_as_float(o[1] << 16) * sw[w];
-            v[t][3] += __uint_as_float(o[1] & 0xFFFF0000u) * sw[w];
-        }
+        for (int w = 0; w < 4; ++w)
+            v[t] += *(const lds_f32x4*)(uintptr_t)(lds0 + (unsigned)(2 * w) * kSlotA + tile0 + 1024u * t) * sw[w];
     }
     // tile 8 wave + t holds dims 128 wave + 16 t + 4 g .. + 4 of the lane's row
     if (nsplit == 1) {
