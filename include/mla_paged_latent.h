@@ -180,6 +180,23 @@ int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, i
                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Host-only check of the contract the decode calls place on their device
+ * inputs, on host copies of them: 0 <= cache_seqlens[b] <= 64 * max_blocks and
+ * block_table[b][j] in [0, nblocks) for every j < ceil(cache_seqlens[b] / 64).
+ * Returns MLA_OK, or MLA_ERR_INVALID_ARG with *bad_seq (if not NULL) set to the
+ * first sequence that breaks it (-1 when all hold). No HIP call.
+ * The decode kernels never read outside kcache or the table even when the
+ * contract is broken (an entry outside [0, nblocks), or an index past the
+ * table, reads block 0; the append calls skip such rows), but the results of
+ * the sequences concerned are then unspecified. With the environment variable
+ * MLA_DEBUG_CHECK set (and not "0"), mla_decode_fwd, mla_decode_fwd_splits and
+ * mla_decode_fp8_fwd copy cache_seqlens and block_table to the host and apply
+ * this check before enqueueing anything (synchronising; for debugging only).
+ */
+int mla_check_inputs_host(const int32_t* cache_seqlens, int batch, const int32_t* block_table, int max_blocks,
+                          int64_t nblocks, int* bad_seq);
+
+/*
  * mla_decode_fwd without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Arguments, results and checks are those

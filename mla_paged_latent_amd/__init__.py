@@ -60,6 +60,8 @@ def load_library(path: Path | str | None = None):
         getattr(lib, name).argtypes = dec
     lib.mla_decode_fwd_noalloc.restype = i32
     lib.mla_decode_fwd_noalloc.argtypes = dec[:16] + [vp]
+    lib.mla_check_inputs_host.restype = i32
+    lib.mla_check_inputs_host.argtypes = [vp, i32, vp, i32, i64, ctypes.POINTER(i32)]
     lib.mla_combine_splits.restype = i32
     lib.mla_combine_splits.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.mla_sparse_plan_sizes.restype = i32
@@ -272,6 +274,21 @@ def mla_combine_splits(num_splits, s_q: int, h_q: int, num_units: int, out, lse,
             num_splits.data_ptr(), B, s_q, h_q, num_units, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
             int(workspace.numel()), _stream(torch)))
     return out, lse
+
+
+def mla_check_inputs_host(cache_seqlens, block_table, nblocks: int):
+    """Check the decode calls' contract on host arrays (numpy): 0 <= L_b <= 64 * max_blocks and
+    every used table entry in [0, nblocks). Returns -1 when it holds, else the first bad sequence."""
+    lens = np.ascontiguousarray(np.asarray(cache_seqlens), dtype=np.int32)
+    table = np.ascontiguousarray(np.asarray(block_table), dtype=np.int32)
+    if table.ndim != 2 or table.shape[0] != lens.shape[0]:
+        raise ValueError("block_table must be [B, max_blocks] and cache_seqlens [B]")
+    bad = ctypes.c_int(-2)
+    rc = load_library().mla_check_inputs_host(lens.ctypes.data, int(lens.shape[0]), table.ctypes.data,
+                                              int(table.shape[1]), int(nblocks), ctypes.byref(bad))
+    if rc != MLA_OK and bad.value < 0:
+        raise MLAError("mla_check_inputs_host", rc)
+    return bad.value
 
 
 def mla_sparse_plan_sizes(batch: int, s_q: int, h_q: int, topk: int, num_cus: int = 0) -> dict:
@@ -527,4 +544,4 @@ __all__ = ["mla_plan_sizes", "mla_workspace_bytes", "mla_get_metadata", "mla_get
            "mla_sparse_plan_sizes", "mla_get_metadata_sparse", "mla_decode_sparse_fwd",
            "mla_fp8_plan_sizes", "mla_get_metadata_fp8", "mla_decode_fp8_fwd", "mla_append_kv_fp8",
            "workspace_bytes", "load_library", "status_string", "MLAError", "LIB_PATH",
-           "D_QK", "D_V", "PAGE_SIZE", "META_INTS"]
+           "D_QK", "D_V", "PAGE_SIZE", "META_INTS", "mla_check_inputs_host"]

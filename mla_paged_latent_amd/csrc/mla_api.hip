@@ -2,8 +2,10 @@
 // launches. Every check runs before anything is enqueued.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/mla_paged_latent.h"
 #include "mla_common.h"
@@ -67,9 +69,53 @@ void workspace_layout(int batch, int rows_total, int num_units, size_t* part_o_b
     *total = *part_o_bytes + round_up(slots * rows_total * sizeof(float), 256);
 }
 
+// The device-side contract of the decode calls on host arrays: 0 <= L_b <=
+// 64 * max_blocks and block_table[b][j] in [0, nblocks) for j < ceil(L_b / 64).
+int check_inputs(const int32_t* seqlens, int batch, const int32_t* table, int max_blocks, int64_t nblocks,
+                 int* bad_seq)
+{
+    for (int b = 0; b < batch; ++b) {
+        const int L = seqlens[b];
+        bool ok = L >= 0 && (int64_t)L <= (int64_t)mla::kPage * max_blocks;
+        for (int j = 0; ok && j < mla::blocks_of(L); ++j) {
+            const int page = table[(size_t)b * max_blocks + j];
+            ok = page >= 0 && page < nblocks;
+        }
+        if (!ok) {
+            if (bad_seq) *bad_seq = b;
+            return MLA_ERR_INVALID_ARG;
+        }
+    }
+    if (bad_seq) *bad_seq = -1;
+    return MLA_OK;
+}
+
+// With MLA_DEBUG_CHECK set (and not "0") in the environment, the decode calls
+// copy cache_seqlens and block_table to the host and check the contract
+// before anything is enqueued (a synchronising copy: for debugging only).
+int debug_check_device_inputs(const int32_t* seqlens, int batch, const int32_t* table, int max_blocks,
+                              int64_t nblocks, hipStream_t stream)
+{
+    const char* env = getenv("MLA_DEBUG_CHECK");
+    if (!env || !env[0] || (env[0] == '0' && !env[1])) return MLA_OK;
+    std::vector<int32_t> lens(batch), tab((size_t)batch * max_blocks);
+    if (hipMemcpyAsync(lens.data(), seqlens, lens.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(tab.data(), table, tab.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return MLA_ERR_HIP;
+    return check_inputs(lens.data(), batch, tab.data(), max_blocks, nblocks, nullptr);
+}
+
 }  // namespace
 
 extern "C" {
+
+int mla_check_inputs_host(const int32_t* cache_seqlens, int batch, const int32_t* block_table, int max_blocks,
+                          int64_t nblocks, int* bad_seq)
+{
+    if (!cache_seqlens || !block_table || batch < 1 || max_blocks < 1 || nblocks < 1) return MLA_ERR_INVALID_ARG;
+    return check_inputs(cache_seqlens, batch, block_table, max_blocks, nblocks, bad_seq);
+}
 
 const char* mla_status_string(int status)
 {
@@ -227,6 +273,8 @@ int mla_decode_fwd(const void* q, const void* kcache, int64_t nblocks, const int
                           workspace_bytes, &p, &geo);
     if (rc != MLA_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
+    rc = debug_check_device_inputs(cache_seqlens, batch, block_table, max_blocks, nblocks, st);
+    if (rc != MLA_OK) return rc;
     if (mla::launch_decode(p, num_units, geo.head_groups, geo.rows_wg, st) != hipSuccess) return MLA_ERR_HIP;
     return run_combine(p, st);
 }
@@ -242,6 +290,8 @@ int mla_decode_fwd_splits(const void* q, const void* kcache, int64_t nblocks, co
     int rc = setup_decode(q, kcache, nblocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
                           softmax_scale, causal, tile_meta, num_splits, num_units, out, lse, workspace,
                           workspace_bytes, &p, &geo);
+    if (rc != MLA_OK) return rc;
+    rc = debug_check_device_inputs(cache_seqlens, batch, block_table, max_blocks, nblocks, (hipStream_t)stream);
     if (rc != MLA_OK) return rc;
     if (mla::launch_decode(p, num_units, geo.head_groups, geo.rows_wg, (hipStream_t)stream) != hipSuccess)
         return MLA_ERR_HIP;
@@ -513,6 +563,8 @@ int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, i
     p.sq_real = 1;
     p.kscale = kscale;
     hipStream_t st = (hipStream_t)stream;
+    rc = debug_check_device_inputs(cache_seqlens, batch, block_table, max_blocks, nblocks, st);
+    if (rc != MLA_OK) return rc;
     if (mla::launch_decode_fp8(p, num_units, geo.head_groups, geo.rows_wg, st) != hipSuccess) return MLA_ERR_HIP;
     return run_combine(p, st);
 }

@@ -27,7 +27,7 @@ namespace {
 typedef unsigned u32x4a __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2a __attribute__((ext_vector_type(2)));
 
-__global__ __launch_bounds__(256) void append_kernel(uint16_t* __restrict__ kcache,
+__global__ __launch_bounds__(256) void append_kernel(uint16_t* __restrict__ kcache, int64_t nblocks,
                                                      const int32_t* __restrict__ block_table, int max_blocks,
                                                      const int32_t* __restrict__ seqlens,
                                                      const uint16_t* __restrict__ rows, int batch, int s_new)
@@ -39,7 +39,9 @@ __global__ __launch_bounds__(256) void append_kernel(uint16_t* __restrict__ kcac
     const int i = (int)(r - (long)b * s_new);
     const int pos = seqlens[b] - s_new + i;                      // its token position
     if (pos < 0) return;                                         // sequence shorter than s_new
+    if ((pos >> 6) >= max_blocks) return;                        // past the table: not written
     const int page = block_table[(size_t)b * max_blocks + (pos >> 6)];
+    if (page < 0 || page >= nblocks) return;                     // not a block of the cache: not written
     const u32x4a* src = (const u32x4a*)(rows + (size_t)r * kDqk);
     u32x4a* dst = (u32x4a*)(kcache + ((size_t)page * kPage + (pos & (kPage - 1))) * kDqk);
     const u32x4a a = src[lane];
@@ -56,6 +58,7 @@ __global__ __launch_bounds__(256) void append_kernel(uint16_t* __restrict__ kcac
 // to E4M3 by the hardware (round to nearest even; |x * 448 / amax| <= 448 so
 // nothing saturates). A zero row gets scale 0 and codes 0.
 __global__ __launch_bounds__(256) void append_fp8_kernel(unsigned char* __restrict__ codes, float* __restrict__ scales,
+                                                         int64_t nblocks,
                                                          const int32_t* __restrict__ block_table, int max_blocks,
                                                          const int32_t* __restrict__ seqlens,
                                                          const uint16_t* __restrict__ rows, int batch, int s_new)
@@ -66,8 +69,9 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(unsigned char* __restri
     const int b = (int)(r / s_new);
     const int i = (int)(r - (long)b * s_new);
     const int pos = seqlens[b] - s_new + i;
-    if (pos < 0) return;
+    if (pos < 0 || (pos >> 6) >= max_blocks) return;
     const int page = block_table[(size_t)b * max_blocks + (pos >> 6)];
+    if (page < 0 || page >= nblocks) return;
     const size_t drow = (size_t)page * kPage + (pos & (kPage - 1));
     const u32x4a* src = (const u32x4a*)(rows + (size_t)r * kDqk);
     const u32x4a a = src[lane];
@@ -125,8 +129,8 @@ int mla_append_kv(void* kcache, int64_t nblocks, const int32_t* block_table, int
     const long rows = (long)batch * s_new;
     if (rows > (long)0x7fffffff * 4 - 4) return MLA_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((rows + 3) / 4));
-    hipLaunchKernelGGL(mla::append_kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint16_t*)kcache, block_table,
-                       max_blocks, cache_seqlens, (const uint16_t*)new_rows, batch, s_new);
+    hipLaunchKernelGGL(mla::append_kernel, grid, dim3(256), 0, (hipStream_t)stream, (uint16_t*)kcache, nblocks,
+                       block_table, max_blocks, cache_seqlens, (const uint16_t*)new_rows, batch, s_new);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -140,7 +144,8 @@ int mla_append_kv_fp8(void* codes, float* scales, int64_t nblocks, const int32_t
     if (rows > (long)0x7fffffff * 4 - 4) return MLA_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((rows + 3) / 4));
     hipLaunchKernelGGL(mla::append_fp8_kernel, grid, dim3(256), 0, (hipStream_t)stream, (unsigned char*)codes,
-                       scales, block_table, max_blocks, cache_seqlens, (const uint16_t*)new_rows, batch, s_new);
+                       scales, nblocks, block_table, max_blocks, cache_seqlens, (const uint16_t*)new_rows, batch,
+                       s_new);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     int K = nsub > wave ? (nsub - wave + 3) >> 2 : 0;         // this wave's sub-tiles: wave, wave+4, ...
     const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
     const int npages = j1 - j0;
-    const int page_vec = (!SPARSE && lane < npages) ? table[j0 + lane] : 0;
+    const int page_vec = (!SPARSE && lane < npages && j0 + lane < p.max_blocks) ? table[j0 + lane] : 0;
     const unsigned rowtab = lds0 + kLdsA;                   // SPARSE: int32 per listed token of the unit
     int fallback = 0;                                       // SPARSE: cache row for padding entries
     if constexpr (SPARSE) {
@@ -262,7 +262,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
             return;
         }
         const int pidx = (tok >> 6) - j0;
-        const int page = pidx < 64 ? __builtin_amdgcn_readlane(page_vec, pidx) : sload(table + j0 + pidx);
+        const int page = safe_page(pidx < 64 ? __builtin_amdgcn_readlane(page_vec, pidx)
+                                             : (j0 + pidx < p.max_blocks ? sload(table + j0 + pidx) : 0),
+                                   p.nblocks);
         const unsigned char* gbase = (const unsigned char*)p.kcache + (size_t)page * kPageBytes +
                                      (size_t)(tok & 63) * kRowBytes;
         copy_rows(gbase, min(16, tok_end - tok), slot0 + (unsigned)(k & 1) * kSlotA, 0, 1, kDmaA, lane);
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
     const int K = nsub > wave ? (nsub - wave + 3) >> 2 : 0;   // this wave's sub-tiles: wave, wave+4, ...
     const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
     const int npages = j1 - j0;
-    const int page_vec = lane < npages ? table[j0 + lane] : 0;
+    const int page_vec = (lane < npages && j0 + lane < p.max_blocks) ? table[j0 + lane] : 0;
     const unsigned char* codes = (const unsigned char*)p.kcache;
 
     float mrun = -INFINITY, lrun = 0.f;
@@ -439,7 +441,9 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
     auto issue = [&](int k) {
         const int tok = tok_begin + 32 * (wave + 4 * k);
         const int pidx = (tok >> 6) - j0;
-        const int page = pidx < 64 ? __builtin_amdgcn_readlane(page_vec, pidx) : sload(table + j0 + pidx);
+        const int page = safe_page(pidx < 64 ? __builtin_amdgcn_readlane(page_vec, pidx)
+                                             : (j0 + pidx < p.max_blocks ? sload(table + j0 + pidx) : 0),
+                                   p.nblocks);
         const size_t row0 = (size_t)page * kPage + (size_t)(tok & 63);
         const unsigned char* gbase = codes + row0 * kDqk;
         const unsigned char* sbase = (const unsigned char*)(p.kscale + row0);

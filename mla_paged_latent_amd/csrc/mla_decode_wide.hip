@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     Segment is = next_segment(p, b0, b0, j0, b1, j1);      // copy cursor
     if (is.b >= p.batch) return;
     int itok = is.tb;
-    int ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
+    int ipage = table_page(p, is.b, itok >> 6);
     Segment cs = is;                                        // compute cursor
 
     // This wave's copies of a block: copy i = wave + 4k of each half (36 per
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
             is = next_segment(p, is.b + 1, b0, j0, b1, j1);
             itok = is.tb;
         }
-        if (is.b < p.batch) ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
+        if (is.b < p.batch) ipage = table_page(p, is.b, itok >> 6);
     };
     // Copy the next block all at once. Rows past the segment's end are copied
     // from the block's first row (finite data, masked to p = 0).

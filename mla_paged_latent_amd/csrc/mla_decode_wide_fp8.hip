@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
     Segment is = next_segment(p, b0, b0, j0, b1, j1);   // copy cursor
     if (is.b >= p.batch) return;
     int itok = is.tb;
-    int ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
+    int ipage = table_page(p, is.b, itok >> 6);
     Segment cs = is;                                       // compute cursor
 
     // this wave copies c = wave + 4k of each block (10 copies for waves 0-1, 9 for 2-3);
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
             is = next_segment(p, is.b + 1, b0, j0, b1, j1);
             itok = is.tb;
         }
-        if (is.b < p.batch) ipage = cload(p.block_table + (size_t)is.b * p.max_blocks + (itok >> 6));
+        if (is.b < p.batch) ipage = table_page(p, is.b, itok >> 6);
     };
     {
         const int valid = is.te - itok;

@@ -162,11 +162,23 @@ __device__ __forceinline__ unsigned short bf16_rne(float f)
     return (unsigned short)(u >> 16);
 }
 
+// A block-table entry as the decode kernels use it: entries outside [0, nblocks)
+// read block 0 instead, so a table that breaks the contract never makes a
+// kernel read outside the cache (the sequence's result is then unspecified).
+__device__ __forceinline__ int safe_page(int page, int64_t nblocks) { return (page >= 0 && page < nblocks) ? page : 0; }
+
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b)
 {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// Block j of sequence b from the block table (wave-uniform); an index past
+// the table or an entry outside [0, nblocks) gives block 0.
+__device__ __forceinline__ int table_page(const DecodeParams& p, int b, int j)
+{
+    return j < p.max_blocks ? safe_page(cload(p.block_table + (size_t)b * p.max_blocks + j), p.nblocks) : 0;
 }
 
 // ---------------------------------------------------------------- units of the cost-line plan

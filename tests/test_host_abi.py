@@ -236,3 +236,27 @@ def test_noalloc_decode_refuses_more_than_its_scratch_before_any_hip_call(lib):
     assert call(q=None) == MLA_ERR_INVALID_ARG
     assert call(h_q=15) == MLA_ERR_UNSUPPORTED
     assert call(units=2) == MLA_ERR_INVALID_ARG
+
+
+def test_check_inputs_host_accepts_the_workloads_and_names_the_first_bad_sequence(lib):
+    import workloads as wl
+    for name in wl.WORKLOADS:
+        inp = wl.make_workload(name, poison=False)
+        assert mla.mla_check_inputs_host(inp.cache_seqlens, inp.block_table, inp.kcache.shape[0]) == -1, name
+    inp = wl.make_workload("memory_bound", poison=False)
+    nb = inp.kcache.shape[0]
+    lens, table = inp.cache_seqlens.copy(), inp.block_table.copy()
+    used = (lens + 63) // 64
+    # entries past each sequence's last block are never read: -1 there is fine (the recipe pads with -1)
+    assert (table[0, used[0]:] == -1).all() or used[0] == table.shape[1]
+    for b, bad in ((3, -1), (5, nb), (9, 1 << 30)):
+        t = table.copy()
+        t[b, used[b] - 1] = bad
+        assert mla.mla_check_inputs_host(lens, t, nb) == b
+    l2 = lens.copy()
+    l2[7] = 64 * table.shape[1] + 1                     # longer than the table can hold
+    assert mla.mla_check_inputs_host(l2, table, nb) == 7
+    l2 = lens.copy()
+    l2[2] = -5
+    assert mla.mla_check_inputs_host(l2, table, nb) == 2
+    assert mla.mla_check_inputs_host(lens, table, int(table.max())) == int(np.argmax((table == table.max()).any(1)))
