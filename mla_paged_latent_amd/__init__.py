@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import contextlib
 import ctypes
+import os
 from pathlib import Path
 
 import numpy as np
@@ -38,7 +39,8 @@ def load_library(path: Path | str | None = None):
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = Path(path) if path is not None else LIB_PATH
+    # MLA_LIB names another build of the same sources (the tests' sanitizer build of the host code)
+    p = Path(path) if path is not None else Path(os.environ.get("MLA_LIB") or LIB_PATH)
     if not p.exists():
         raise RuntimeError("HIP library %s is not built; run `python -m mla_paged_latent_amd.build`" % p)
     lib = ctypes.CDLL(str(p))

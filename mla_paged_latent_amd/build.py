@@ -48,9 +48,9 @@ def sources():
     return sorted(CSRC.glob("*.hip"))
 
 
-def build(verbose: bool = False, out: Path = LIB, extra_flags=()) -> Path:
+def build(verbose: bool = False, out: Path = LIB, extra_flags=(), objdir: Path | None = None) -> Path:
     """Compile and link; always rebuilds. Returns the library path."""
-    objdir = ROOT / "_build" / "obj"
+    objdir = Path(objdir) if objdir is not None else ROOT / "_build" / "obj"
     objdir.mkdir(parents=True, exist_ok=True)
     objs = []
     cc = hipcc()

@@ -44,8 +44,12 @@ def load(path: Path | None = None):
     else:
         if _lib is not None:
             return _lib
-        build()
-        lib = ctypes.CDLL(str(_LIB))
+        alt = os.environ.get("MLA_ORACLE_LIB")    # a sanitizer build of the same sources (tests)
+        if alt:
+            lib = ctypes.CDLL(alt)
+        else:
+            build()
+            lib = ctypes.CDLL(str(_LIB))
     fn = lib.mla_oracle_decode
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
