@@ -354,6 +354,46 @@ def bench_append(args, torch, mla, dev):
     return 0
 
 
+def graph_ms(torch, fn, n):
+    """fn(0), ..., fn(n - 1) captured in one HIP graph (on a side stream), replayed once,
+    then one replay timed with events on the current stream: ms per call."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for k in range(n):
+            fn(k)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def kernel_roofline(mla, name, lens, h_q, s_q, units, nbytes, flops, kern_ms, traffic, plan_h_q=None):
+    """Roofline entry of a decode kernel timed alone (a *_splits call): out/lse of the
+    sequences (lists) the plan splits are the combine kernel's bytes, not the kernel's.
+    plan_h_q: the head count whose geometry the plan used (sparse plans: 16-row units)."""
+    _, host_splits = mla.mla_get_metadata_host(lens, plan_h_q or h_q, s_q, units)
+    split_rows = int((np.diff(host_splits) > 1).sum()) * s_q * h_q
+    kb = nbytes - split_rows * (2 * wl.D_V + 4)
+    k_gbs = kb / (kern_ms * 1e-3) / 1e9
+    k_tf = flops / (kern_ms * 1e-3) / 1e12
+    r = {"bound": "hbm", "kernel": name, "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel_alg_bytes": kb,
+         "kernel_ms_avg": round(kern_ms, 6), "kernel_tflops": round(k_tf, 3),
+         "kernel_mfma_frac": round(k_tf / BF16_PEAK_TFLOPS, 5)}
+    if flops / nbytes >= BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        # above the ridge (the matrix ops run in bf16): judged against the bf16 matrix peak
+        r.update({"bound": "mfma", "achieved": round(k_tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(k_tf / BF16_PEAK_TFLOPS, 5), "kernel_gbs": round(k_gbs, 2),
+                  "kernel_hbm_frac": round(k_gbs / HBM_PEAK_GBS, 4)})
+    return r
+
+
 def bench_sparse(args, torch, mla, dev):
     """Sparse decode: plan (mla_get_metadata_sparse) + mla_decode_sparse_fwd per step."""
     sp = wl.make_sparse()
@@ -403,6 +443,12 @@ def bench_sparse(args, torch, mla, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+
+    def decode_only(k):
+        kc, q = reps[k % R]
+        mla.mla_decode_sparse_fwd_splits(q, kc, table, idx, lens, d.softmax_scale, meta, splits, out=out, lse=lse,
+                                         workspace=ws)
+    kern_ms = graph_ms(torch, decode_only, args.steps)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
     result = {
@@ -413,10 +459,10 @@ def bench_sparse(args, torch, mla, dev):
         "config": {"workload": "sparse: " + wl.SPARSE_DESCRIPTION + ", d_qk=576, d_v=512, block 64, shuffled "
                                "block_table, bf16 N(0,1), scale 1/sqrt(192)",
                    "batch": B, "s_q": s_q, "h_q": h_q, "topk": topk, "replicas": R, "num_units": units},
+        "step": "mla_get_metadata_sparse + mla_decode_sparse_fwd (plan, decode kernel, split combine)",
         "tflops": round(tf, 3), "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
-        "roofline": {"bound": "hbm", "kernel": "sparse decode step (plan + decode + combine)", "achieved": round(gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("sparse"), "kernel_ms_avg": round(ms, 6)},
+        "roofline": kernel_roofline(mla, "sparse decode kernel (mla_decode_sparse_fwd_splits)", sp.counts, h_q, 1,
+                                    units, nbytes, flops, kern_ms, measured_traffic("sparse"), plan_h_q=16),
     }
     if not args.no_cpu_baseline:
         import oracle as orc
@@ -495,6 +541,13 @@ def bench_fp8(args, torch, mla, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+
+    def decode_only(k):
+        c, sc, q, tab, ln = reps[k % R]
+        meta, splits = plans[k % R]
+        mla.mla_decode_fp8_fwd_splits(q, c, sc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal,
+                                      out=out, lse=lse, workspace=ws)
+    kern_ms = graph_ms(torch, decode_only, args.steps)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
     result = {
@@ -507,15 +560,11 @@ def bench_fp8(args, torch, mla, dev):
                                % (args.workload, wl.DESCRIPTIONS[args.workload]),
                    "batch": B, "s_q": s_q, "h_q": h_q, "tokens": int(inp.cache_seqlens.sum()), "replicas": R,
                    "num_units": units},
+        "step": "mla_get_metadata_fp8 + mla_decode_fp8_fwd (plan, decode kernel, split combine)",
         "tflops": round(tf, 3), "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
-        "roofline": {"bound": "hbm", "kernel": "fp8 decode step (plan + decode + combine)", "achieved": round(gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("fp8_" + args.workload), "kernel_ms_avg": round(ms, 6)},
+        "roofline": kernel_roofline(mla, "FP8 decode kernel (mla_decode_fp8_fwd_splits)", inp.cache_seqlens, h_q,
+                                    s_q, units, nbytes, flops, kern_ms, measured_traffic("fp8_" + args.workload)),
     }
-    if flops / nbytes >= BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        # above the ridge (the matrix ops run in bf16): judged against the bf16 matrix peak
-        result["roofline"].update({"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
-                                   "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 5), "gbs": round(gbs, 2)})
     if not args.no_cpu_baseline:
         import oracle as orc
         from oracle import fp8 as ofp8

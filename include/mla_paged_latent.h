@@ -189,9 +189,10 @@ int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, i
  * contract is broken (an entry outside [0, nblocks), or an index past the
  * table, reads block 0; the append calls skip such rows), but the results of
  * the sequences concerned are then unspecified. With the environment variable
- * MLA_DEBUG_CHECK set (and not "0"), mla_decode_fwd, mla_decode_fwd_splits and
- * mla_decode_fp8_fwd copy cache_seqlens and block_table to the host and apply
- * this check before enqueueing anything (synchronising; for debugging only).
+ * MLA_DEBUG_CHECK set (and not "0"), mla_decode_fwd, mla_decode_fwd_splits,
+ * mla_decode_fp8_fwd and mla_decode_fp8_fwd_splits copy cache_seqlens and
+ * block_table to the host and apply this check before enqueueing anything
+ * (synchronising; for debugging only).
  */
 int mla_check_inputs_host(const int32_t* cache_seqlens, int batch, const int32_t* block_table, int max_blocks,
                           int64_t nblocks, int* bad_seq);
@@ -242,6 +243,11 @@ int mla_decode_fwd_noalloc(const void* q, const void* kcache, int64_t nblocks,
  *   Contracts the host cannot check: 0 <= topk_lens[.] <= topk; a listed
  *   position t has a valid block block_table[b][t / 64] (entries with t / 64
  *   >= max_blocks or a negative table entry are treated as padding).
+ * mla_decode_sparse_fwd_splits: the decode kernel of mla_decode_sparse_fwd
+ *   alone (same arguments and checks), as mla_decode_fwd_splits is for
+ *   mla_decode_fwd: mla_decode_sparse_fwd is exactly it followed by
+ *   mla_combine_splits(num_splits, batch * s_q, 1, h_q, num_units, out, lse,
+ *   workspace, workspace_bytes, stream) on the same stream.
  * Errors: as for mla_plan_sizes / mla_get_metadata / mla_decode_fwd
  *   (MLA_ERR_UNSUPPORTED for topk > 2048, h_q not a multiple of 16).
  */
@@ -256,6 +262,13 @@ int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks,
                           const int32_t* tile_meta, const int32_t* num_splits, int num_units,
                           void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
+int mla_decode_sparse_fwd_splits(const void* q, const void* kcache, int64_t nblocks,
+                                 const int32_t* block_table, int max_blocks,
+                                 const int32_t* indices, const int32_t* topk_lens, int topk,
+                                 int batch, int s_q, int h_q, float softmax_scale,
+                                 const int32_t* tile_meta, const int32_t* num_splits, int num_units,
+                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /*
  * FP8 latent cache: cached rows stored as 8-bit floats with one float32 scale
@@ -274,6 +287,9 @@ int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks,
  *   exactly what mla_plan_sizes / mla_get_metadata return.
  * mla_decode_fp8_fwd: as mla_decode_fwd with kcache replaced by (kcodes,
  *   kscale); both 16-byte aligned.
+ * mla_decode_fp8_fwd_splits: its decode kernel alone (same arguments and
+ *   checks); mla_decode_fp8_fwd is exactly it followed by mla_combine_splits
+ *   with the same batch, s_q, h_q, plan and workspace on the same stream.
  * mla_append_kv_fp8: as mla_append_kv, but each new bf16 row is quantized
  *   into the FP8 cache: amax = its largest magnitude, scale = amax / 448 and
  *   code = E4M3 nearest (ties to even) to x * (448 / amax), the two quotients
@@ -293,6 +309,13 @@ int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, i
                        const int32_t* tile_meta, const int32_t* num_splits, int num_units,
                        void* out, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream);
+int mla_decode_fp8_fwd_splits(const void* q, const void* kcodes, const float* kscale, int64_t nblocks,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* cache_seqlens, int batch, int s_q, int h_q,
+                              float softmax_scale, int causal,
+                              const int32_t* tile_meta, const int32_t* num_splits, int num_units,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
 int mla_append_kv_fp8(void* kcodes, float* kscale, int64_t nblocks, const int32_t* block_table, int max_blocks,
                       const int32_t* cache_seqlens, const void* new_rows, int batch, int s_new, void* stream);
 

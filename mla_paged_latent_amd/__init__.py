@@ -71,17 +71,19 @@ def load_library(path: Path | str | None = None):
                                           ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.mla_get_metadata_sparse.restype = i32
     lib.mla_get_metadata_sparse.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
-    lib.mla_decode_sparse_fwd.restype = i32
-    lib.mla_decode_sparse_fwd.argtypes = [vp, vp, i64, vp, i32, vp, vp, i32, i32, i32, i32, ctypes.c_float,
-                                          vp, vp, i32, vp, vp, vp, sz, vp]
+    for name in ("mla_decode_sparse_fwd", "mla_decode_sparse_fwd_splits"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [vp, vp, i64, vp, i32, vp, vp, i32, i32, i32, i32, ctypes.c_float,
+                                       vp, vp, i32, vp, vp, vp, sz, vp]
     lib.mla_fp8_plan_sizes.restype = i32
     lib.mla_fp8_plan_sizes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(sz),
                                        ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.mla_get_metadata_fp8.restype = i32
     lib.mla_get_metadata_fp8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
-    lib.mla_decode_fp8_fwd.restype = i32
-    lib.mla_decode_fp8_fwd.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, i32,
-                                       vp, vp, vp, sz, vp]
+    for name in ("mla_decode_fp8_fwd", "mla_decode_fp8_fwd_splits"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp,
+                                       i32, vp, vp, vp, sz, vp]
     lib.mla_append_kv_fp8.restype = i32
     lib.mla_append_kv_fp8.argtypes = [vp, vp, i64, vp, i32, vp, vp, i32, i32, vp]
     lib.mla_append_kv.restype = i32
@@ -331,6 +333,22 @@ def mla_decode_sparse_fwd(q, kcache, block_table, indices, topk_lens, softmax_sc
     """Sparse decode: q bf16 [B, s_q, h_q, 576] attends, per new token, over the
     cached positions indices[b, i, :topk_lens[b*s_q+i]] (int32 [B, s_q, topk];
     entries < 0 are padding). Returns (out bf16 [B, s_q, h_q, 512], lse f32 [B, s_q, h_q])."""
+    out, lse, _ = _sparse_call("mla_decode_sparse_fwd", q, kcache, block_table, indices, topk_lens, softmax_scale,
+                               tile_meta, num_splits, out, lse, workspace)
+    return out, lse
+
+
+def mla_decode_sparse_fwd_splits(q, kcache, block_table, indices, topk_lens, softmax_scale: float, tile_meta,
+                                 num_splits, out=None, lse=None, workspace=None):
+    """The decode kernel of mla_decode_sparse_fwd alone: unsplit lists get out/lse, split
+    ones leave partials in workspace (merged by mla_combine_splits with B * s_q lists of
+    one new token). Returns (out, lse, workspace)."""
+    return _sparse_call("mla_decode_sparse_fwd_splits", q, kcache, block_table, indices, topk_lens, softmax_scale,
+                        tile_meta, num_splits, out, lse, workspace)
+
+
+def _sparse_call(name, q, kcache, block_table, indices, topk_lens, softmax_scale, tile_meta, num_splits, out, lse,
+                 workspace):
     import torch
     _need(q, torch.bfloat16, "q")
     dev = q.device
@@ -362,12 +380,12 @@ def mla_decode_sparse_fwd(q, kcache, block_table, indices, topk_lens, softmax_sc
             _check("mla_workspace_bytes", load_library().mla_workspace_bytes(B * s_q, 1, h_q, num_units,
                                                                               ctypes.byref(n)))
             workspace = torch.empty((max(ws, n.value, 16),), dtype=torch.uint8, device=dev)
-        _check("mla_decode_sparse_fwd", load_library().mla_decode_sparse_fwd(
+        _check(name, getattr(load_library(), name)(
             q.data_ptr(), kcache.data_ptr(), int(kcache.shape[0]), block_table.data_ptr(), int(block_table.shape[1]),
             indices.data_ptr(), topk_lens.data_ptr(), topk, B, s_q, h_q, float(softmax_scale), tile_meta.data_ptr(),
             num_splits.data_ptr(), num_units, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
             int(workspace.numel()), _stream(torch)))
-    return out, lse
+    return out, lse, workspace
 
 
 def mla_fp8_plan_sizes(batch: int, s_q: int, h_q: int, num_cus: int = 0) -> dict:
@@ -405,6 +423,21 @@ def mla_decode_fp8_fwd(q, kcodes, kscale, block_table, cache_seqlens, softmax_sc
                        causal: bool = True, out=None, lse=None, workspace=None):
     """Decode over an FP8 cache: kcodes uint8 [nblocks, 64, 576] (E4M3), kscale float32
     [nblocks, 64]; the rest as mla_decode_fwd. Returns (out, lse)."""
+    out, lse, _ = _fp8_call("mla_decode_fp8_fwd", q, kcodes, kscale, block_table, cache_seqlens, softmax_scale,
+                            tile_meta, num_splits, causal, out, lse, workspace)
+    return out, lse
+
+
+def mla_decode_fp8_fwd_splits(q, kcodes, kscale, block_table, cache_seqlens, softmax_scale: float, tile_meta,
+                              num_splits, causal: bool = True, out=None, lse=None, workspace=None):
+    """The decode kernel of mla_decode_fp8_fwd alone (mla_combine_splits merges the split
+    sequences' partials). Returns (out, lse, workspace)."""
+    return _fp8_call("mla_decode_fp8_fwd_splits", q, kcodes, kscale, block_table, cache_seqlens, softmax_scale,
+                     tile_meta, num_splits, causal, out, lse, workspace)
+
+
+def _fp8_call(name, q, kcodes, kscale, block_table, cache_seqlens, softmax_scale, tile_meta, num_splits, causal, out,
+              lse, workspace):
     import torch
     _need(q, torch.bfloat16, "q")
     dev = q.device
@@ -432,12 +465,12 @@ def mla_decode_fp8_fwd(q, kcodes, kscale, block_table, cache_seqlens, softmax_sc
         if workspace is None:
             ws = max(mla_fp8_plan_sizes(B, s_q, h_q)["workspace_bytes"], workspace_bytes(B, s_q, h_q, num_units))
             workspace = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
-        _check("mla_decode_fp8_fwd", load_library().mla_decode_fp8_fwd(
+        _check(name, getattr(load_library(), name)(
             q.data_ptr(), kcodes.data_ptr(), kscale.data_ptr(), int(kcodes.shape[0]), block_table.data_ptr(),
             int(block_table.shape[1]), cache_seqlens.data_ptr(), B, s_q, h_q, float(softmax_scale),
             1 if causal else 0, tile_meta.data_ptr(), num_splits.data_ptr(), num_units, out.data_ptr(),
             lse.data_ptr(), workspace.data_ptr(), int(workspace.numel()), _stream(torch)))
-    return out, lse
+    return out, lse, workspace
 
 
 def mla_append_kv_fp8(kcodes, kscale, block_table, cache_seqlens, new_rows):
@@ -546,4 +579,5 @@ __all__ = ["mla_plan_sizes", "mla_workspace_bytes", "mla_get_metadata", "mla_get
            "mla_sparse_plan_sizes", "mla_get_metadata_sparse", "mla_decode_sparse_fwd",
            "mla_fp8_plan_sizes", "mla_get_metadata_fp8", "mla_decode_fp8_fwd", "mla_append_kv_fp8",
            "workspace_bytes", "load_library", "status_string", "MLAError", "LIB_PATH",
-           "D_QK", "D_V", "PAGE_SIZE", "META_INTS", "mla_check_inputs_host"]
+           "D_QK", "D_V", "PAGE_SIZE", "META_INTS", "mla_check_inputs_host", "mla_decode_sparse_fwd_splits",
+           "mla_decode_fp8_fwd_splits"]

@@ -449,11 +449,15 @@ int mla_get_metadata_sparse(const int32_t* topk_lens, int batch, int s_q, int h_
     return MLA_OK;
 }
 
-int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table,
-                          int max_blocks, const int32_t* indices, const int32_t* topk_lens, int topk, int batch,
-                          int s_q, int h_q, float softmax_scale, const int32_t* tile_meta,
-                          const int32_t* num_splits, int num_units, void* out, float* lse, void* workspace,
-                          size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// The sparse decode kernel, then (with `combine`) the split combine.
+int decode_sparse(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table, int max_blocks,
+                  const int32_t* indices, const int32_t* topk_lens, int topk, int batch, int s_q, int h_q,
+                  float softmax_scale, const int32_t* tile_meta, const int32_t* num_splits, int num_units, void* out,
+                  float* lse, void* workspace, size_t workspace_bytes, void* stream, bool combine)
 {
     int rc = check_sparse_shape(batch, s_q, h_q, topk);
     if (rc != MLA_OK) return rc;
@@ -494,7 +498,33 @@ int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks, co
     p.kscale = nullptr;
     hipStream_t st = (hipStream_t)stream;
     if (mla::launch_decode_sparse(p, num_units, h_q / 16, st) != hipSuccess) return MLA_ERR_HIP;
-    return run_combine(p, st);
+    return combine ? run_combine(p, st) : MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_sparse_fwd(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table,
+                          int max_blocks, const int32_t* indices, const int32_t* topk_lens, int topk, int batch,
+                          int s_q, int h_q, float softmax_scale, const int32_t* tile_meta,
+                          const int32_t* num_splits, int num_units, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    return decode_sparse(q, kcache, nblocks, block_table, max_blocks, indices, topk_lens, topk, batch, s_q, h_q,
+                         softmax_scale, tile_meta, num_splits, num_units, out, lse, workspace, workspace_bytes, stream,
+                         true);
+}
+
+int mla_decode_sparse_fwd_splits(const void* q, const void* kcache, int64_t nblocks, const int32_t* block_table,
+                                 int max_blocks, const int32_t* indices, const int32_t* topk_lens, int topk,
+                                 int batch, int s_q, int h_q, float softmax_scale, const int32_t* tile_meta,
+                                 const int32_t* num_splits, int num_units, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream)
+{
+    return decode_sparse(q, kcache, nblocks, block_table, max_blocks, indices, topk_lens, topk, batch, s_q, h_q,
+                         softmax_scale, tile_meta, num_splits, num_units, out, lse, workspace, workspace_bytes, stream,
+                         false);
 }
 
 }  // extern "C"
@@ -519,10 +549,15 @@ int mla_get_metadata_fp8(const int32_t* cache_seqlens, int batch, int s_q, int h
     return mla_get_metadata(cache_seqlens, batch, s_q, h_q, num_units, tile_meta, num_splits, stream);
 }
 
-int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, int64_t nblocks,
-                       const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch, int s_q,
-                       int h_q, float softmax_scale, int causal, const int32_t* tile_meta, const int32_t* num_splits,
-                       int num_units, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// The FP8 decode kernel, then (with `combine`) the split combine.
+int decode_fp8(const void* q, const void* kcodes, const float* kscale, int64_t nblocks, const int32_t* block_table,
+               int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, float softmax_scale,
+               int causal, const int32_t* tile_meta, const int32_t* num_splits, int num_units, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream, bool combine)
 {
     int rc = check_shape(batch, s_q, h_q);
     if (rc != MLA_OK) return rc;
@@ -566,7 +601,32 @@ int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, i
     rc = debug_check_device_inputs(cache_seqlens, batch, block_table, max_blocks, nblocks, st);
     if (rc != MLA_OK) return rc;
     if (mla::launch_decode_fp8(p, num_units, geo.head_groups, geo.rows_wg, st) != hipSuccess) return MLA_ERR_HIP;
-    return run_combine(p, st);
+    return combine ? run_combine(p, st) : MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_fp8_fwd(const void* q, const void* kcodes, const float* kscale, int64_t nblocks,
+                       const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch, int s_q,
+                       int h_q, float softmax_scale, int causal, const int32_t* tile_meta, const int32_t* num_splits,
+                       int num_units, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return decode_fp8(q, kcodes, kscale, nblocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                      softmax_scale, causal, tile_meta, num_splits, num_units, out, lse, workspace, workspace_bytes,
+                      stream, true);
+}
+
+int mla_decode_fp8_fwd_splits(const void* q, const void* kcodes, const float* kscale, int64_t nblocks,
+                              const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch,
+                              int s_q, int h_q, float softmax_scale, int causal, const int32_t* tile_meta,
+                              const int32_t* num_splits, int num_units, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    return decode_fp8(q, kcodes, kscale, nblocks, block_table, max_blocks, cache_seqlens, batch, s_q, h_q,
+                      softmax_scale, causal, tile_meta, num_splits, num_units, out, lse, workspace, workspace_bytes,
+                      stream, false);
 }
 
 }  // extern "C"

@@ -84,8 +84,33 @@ def _decode_args(**over):
     (dict(batch=16385), MLA_ERR_UNSUPPORTED),
     (dict(ws_bytes=1024), MLA_ERR_WORKSPACE_TOO_SMALL),
 ])
-def test_decode_rejects_bad_arguments_before_any_launch(lib, over, code):
-    assert lib.mla_decode_fwd(*_decode_args(**over)) == code
+@pytest.mark.parametrize("name", ["mla_decode_fwd", "mla_decode_fwd_splits", "mla_decode_fp8_fwd",
+                                  "mla_decode_fp8_fwd_splits"])
+def test_decode_rejects_bad_arguments_before_any_launch(lib, name, over, code):
+    args = _decode_args(**over)
+    if "fp8" in name:
+        args.insert(2, ctypes.c_void_p(0x20000))          # kscale
+    assert getattr(lib, name)(*args) == code
+
+
+@pytest.mark.parametrize("name", ["mla_decode_sparse_fwd", "mla_decode_sparse_fwd_splits"])
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), MLA_ERR_INVALID_ARG),
+    (dict(indices=None), MLA_ERR_INVALID_ARG),
+    (dict(units=2), MLA_ERR_INVALID_ARG),                        # needs batch * s_q + 1
+    (dict(topk=2049), MLA_ERR_UNSUPPORTED),
+    (dict(h_q=24), MLA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=1024), MLA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_sparse_decode_rejects_bad_arguments_before_any_launch(lib, name, over, code):
+    fake = ctypes.c_void_p(0x10000)
+    a = dict(q=fake, kcache=fake, nblocks=8, block_table=fake, max_blocks=4, indices=fake, lens=fake, topk=64,
+             batch=2, s_q=1, h_q=16, scale=0.07, meta=fake, splits=fake, units=8, out=fake, lse=fake, ws=fake,
+             ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    args = [a[k] for k in ("q", "kcache", "nblocks", "block_table", "max_blocks", "indices", "lens", "topk", "batch",
+                           "s_q", "h_q", "scale", "meta", "splits", "units", "out", "lse", "ws", "ws_bytes", "stream")]
+    assert getattr(lib, name)(*args) == code
 
 
 def test_get_metadata_rejects_bad_arguments(lib):
