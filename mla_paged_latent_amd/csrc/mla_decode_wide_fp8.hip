@@ -12,9 +12,12 @@
 // groups; the partial score tiles are summed through LDS; the token halves
 // exchange row maxima; wave w accumulates output dims [128 w, +128) of all 64
 // rows). What changes is the operand path:
-//  * a block is staged as two 32-token FP8 slots (the layout of the FP8
-//    streaming kernel: 37-chunk rows, the 32 row scales after them), 38 KB
-//    instead of 72 KB, in 38 one-KB copies spread over the QK^T matrix ops;
+//  * a block is staged as two 32-token FP8 slots (the code rows laid out as
+//    in the FP8 streaming kernel: 37-chunk rows), 38 KB instead of 72 KB, in
+//    38 one-KB copies spread over the QK^T matrix ops, and its 64 row scales
+//    go to a 256-byte area of their own in one 16-lane copy, so that every
+//    code copy has the same form (a scalar base plus a lane offset held in
+//    registers);
 //  * K fragments are 8-byte reads of codes turned into bf16 exactly before
 //    the matrix op; V^T fragments come from ds_read_b64_tr_b8 (in each 16-lane
 //    group output lane j byte e is byte j % 8 of source lane 2 e + j / 8), one
@@ -30,21 +33,19 @@ namespace {
 
 constexpr int kF8BlockB = 2 * kF8SlotB;            // 38,912 B: one 64-token block
 constexpr int kXBf = 4096;                          // LDS inbox of each wave
-constexpr int kCopyMapB = 10 * 256;                 // per wave: its copies' lane offsets in a whole block
-constexpr int kLdsF = 2 * kF8BlockB + 4 * kXBf + 4 * kCopyMapB;    // 104,448 B
+constexpr int kScaleB = 256;                        // the 64 row scales of a block
+constexpr int kLdsF = 2 * kF8BlockB + 4 * kXBf + 2 * kScaleB;      // 94,720 B
 constexpr unsigned kXMaxF = 0, kXPF = 128, kXSumF = 2176;
-constexpr unsigned kScaleLane = 0x80000000u;        // copy-map flag: the lane brings row scales
 
 __device__ __forceinline__ float lds_ff(unsigned addr) { return *(const lds_f32*)(uintptr_t)addr; }
 
-// Copy c (0..37) of a block: slot c / 19, copy c % 19 of that slot. Lane map
-// as in the FP8 streaming kernel: position pos of the slot holds chunk ch of
-// slot row r (pp = pos minus the pad chunk before row 16, r = pp / 37 =
-// (pp * 1772) >> 16 exactly for pp < 2367); pad chunks and rows past the
-// `valid` real rows of the block read the block's first row; the last copy of
-// a slot also brings its 32 row scales. Returns the lane's byte offset from
-// the block's first code row, or kScaleLane | the byte offset into the slot's
-// 32 scales.
+// Copy c (0..37) of a block's codes: slot c / 19, copy c % 19 of that slot.
+// Lane map as in the FP8 streaming kernel: position pos of the slot holds
+// chunk ch of slot row r (pp = pos minus the pad chunk before row 16, r = pp /
+// 37 = (pp * 1772) >> 16 exactly for pp < 2367); pad chunks, positions past
+// the last row and rows past the `valid` real rows of the block read the
+// block's first row. Returns the lane's byte offset from the block's first
+// code row.
 __device__ __forceinline__ unsigned f8_copy_offset(int valid, int c, int lane)
 {
     const int hb = c >= 19 ? 1 : 0;
@@ -56,24 +57,16 @@ __device__ __forceinline__ unsigned f8_copy_offset(int valid, int c, int lane)
     const bool data = pos != kF8Row16 - 1 && ch < 36 && r < 32;
     int br = 32 * hb + r;
     br = br < valid ? br : 0;
-    if (i == 18 && pos >= kF8Scale && pos < kF8Scale + 8) return kScaleLane | (unsigned)(16 * (pos - kF8Scale));
     return data ? (unsigned)(br * kDqk + 16 * ch) : 0u;
 }
 
-// Issue copy c of the block at cache row row0 with this lane's offset `off`.
-__device__ __forceinline__ void f8_block_copy(const unsigned char* codes, const float* kscale, size_t row0,
-                                              unsigned off, unsigned dst_block, int c)
+// Issue code copy c of the block at cache row row0 with this lane's offset `off`.
+__device__ __forceinline__ void f8_block_copy(const unsigned char* codes, size_t row0, unsigned off,
+                                              unsigned dst_block, int c)
 {
     const int hb = c >= 19 ? 1 : 0;
     const int i = c - 19 * hb;
-    const unsigned char* gblock = codes + row0 * kDqk;
-    const unsigned dst = dst_block + (unsigned)hb * kF8SlotB + (unsigned)i * 1024u;
-    if (i == 18) {
-        const unsigned char* sb = (const unsigned char*)(kscale + row0 + 32 * hb);
-        dma16((off & kScaleLane) ? sb + (off & 0xFFFFu) : gblock + off, dst);
-    } else {
-        dma16s(gblock, off, dst);
-    }
+    dma16s(codes + row0 * kDqk, off, dst_block + (unsigned)hb * kF8SlotB + (unsigned)i * 1024u);
 }
 
 }  // namespace
@@ -102,6 +95,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
     const float c = p.scale_log2;
     const unsigned xin = lds0 + 2 * kF8BlockB;              // inbox of wave 0
     const unsigned xmine = xin + (unsigned)wave * kXBf;
+    const unsigned scl0 = xin + 4 * kXBf;                   // row scales of LDS block 0 (block 1: + kScaleB)
 
     Segment is = next_segment(p, b0, b0, j0, b1, j1);   // copy cursor
     if (is.b >= p.batch) return;
@@ -109,20 +103,23 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
     int ipage = table_page(p, is.b, itok >> 6);
     Segment cs = is;                                       // compute cursor
 
-    // this wave copies c = wave + 4k of each block (10 copies for waves 0-1, 9 for 2-3);
-    // the lane offsets of a whole block are computed once and kept in LDS
-    const int ncopy = (38 - wave + 3) >> 2;
-    const unsigned cmap = lds0 + 2 * kF8BlockB + 4 * kXBf + (unsigned)wave * kCopyMapB + 4u * (unsigned)lane;
-    for (int k = 0; k < ncopy; ++k)
-        *(__attribute__((address_space(3))) unsigned*)(uintptr_t)(cmap + 256u * k) = f8_copy_offset(kPage, wave + 4 * k, lane);
+    // this wave copies c = wave + 4k of each block's codes (10 copies for waves 0-1,
+    // 9 for 2-3, whose last slot goes to the row scales: wave 2 copies them); the
+    // lane offsets of a whole block are computed once and kept in registers
+    unsigned coff[10];
+#pragma unroll
+    for (int k = 0; k < 10; ++k) coff[k] = f8_copy_offset(kPage, wave + 4 * k, lane);
     int n_issued = 0;
-    // copy k of this wave for the block at the copy cursor; a whole block takes its
-    // lane offset from the map (read by the caller), a partial one computes it
+    // copy k of this wave for the block at the copy cursor (k == ncopy: wave 2's row scales)
     auto copy_one = [&](int k, unsigned off) {
-        f8_block_copy(codes, p.kscale, (size_t)ipage * kPage, off, lds0 + (unsigned)(n_issued & 1) * kF8BlockB,
-                      wave + 4 * k);
+        const size_t row0 = (size_t)ipage * kPage;
+        if (k < 9 || wave < 2) {
+            f8_block_copy(codes, row0, off, lds0 + (unsigned)(n_issued & 1) * kF8BlockB, wave + 4 * k);
+        } else if (wave == 2 && lane < 16) {
+            dma16s((const unsigned char*)(p.kscale + row0), 16u * (unsigned)lane,
+                   scl0 + (unsigned)(n_issued & 1) * kScaleB);
+        }
     };
-    auto map_off = [&](int k) { return *(const __attribute__((address_space(3))) unsigned*)(uintptr_t)(cmap + 256u * k); };
     auto copy_end = [&]() {
         ++n_issued;
         itok += kPage;
@@ -134,7 +131,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
     };
     {
         const int valid = is.te - itok;
-        for (int k = 0; k < ncopy; ++k) copy_one(k, f8_copy_offset(valid, wave + 4 * k, lane));
+        for (int k = 0; k < 10; ++k) copy_one(k, f8_copy_offset(valid, wave + 4 * k, lane));
         copy_end();
     }
 
@@ -187,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
             const bool whole = is.te - itok >= kPage;
             if (more && !whole) {                           // the end of a segment: copied here
                 const int valid = is.te - itok;
-                for (int k = 0; k < ncopy; ++k) copy_one(k, f8_copy_offset(valid, wave + 4 * k, lane));
+                for (int k = 0; k < 10; ++k) copy_one(k, f8_copy_offset(valid, wave + 4 * k, lane));
             }
             const unsigned blk = lds0 + (unsigned)(n & 1) * kF8BlockB;
             const unsigned sb = blk + (unsigned)th * kF8SlotB;
@@ -201,7 +198,6 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
                 u32x2 kv[4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) kv[ks] = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(sb + k_base + 16u * ks);
-                unsigned co[2] = {map_off(0), map_off(1)};  // copy offsets, two k-steps ahead
                 // K fragments are converted one k-step ahead (ping-pong), under the previous matrix ops
                 bf16x8 a2[2];
                 a2[0] = e4m3x8_to_bf16(kv[0]);
@@ -212,20 +208,18 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
                     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[ks & 1], qf[1][ks], s1, 0, 0, 0);
                     if (ks + 1 < 18) a2[(ks + 1) & 1] = e4m3x8_to_bf16(kv[(ks + 1) & 3]);
                     if (ks + 4 < 18) kv[ks & 3] = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(sb + k_base + 16u * (ks + 4));
-                    if (ks < 10) {
-                        if (spread && ks < ncopy) copy_one(ks, co[ks & 1]);
-                        if (ks + 2 < 10) co[ks & 1] = map_off(ks + 2);
-                    }
+                    if (ks < 10 && spread) copy_one(ks, coff[ks]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (more) copy_end();
-            // row scales of the owned tile's tokens (element i: token token_of_row(8(i/4) + 4h + i%4)
-            // of the slot), read here so that their latency passes under the exchange barrier
+            // row scales of the owned tile's tokens (element i: token 32 th + token_of_row(8(i/4) + 4h + i%4)
+            // of the block), read here so that their latency passes under the exchange barrier
             float scl[16];
+            const unsigned sclb = scl0 + (unsigned)(n & 1) * kScaleB + 128u * (unsigned)th;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                scl[i] = lds_ff(sb + 16u * kF8Scale + 4u * (unsigned)token_of_row(8 * (i >> 2) + 4 * h + (i & 3)));
+                scl[i] = lds_ff(sclb + 4u * (unsigned)token_of_row(8 * (i >> 2) + 4 * h + (i & 3)));
             // ---- score exchange: send the partner's row group (s1), add the partner's half of mine (s0)
             f32x16 s = s0;
             {
