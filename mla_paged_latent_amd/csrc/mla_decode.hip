@@ -235,6 +235,19 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     }
 
     const unsigned slot0 = lds0 + (unsigned)(2 * wave) * kSlotA;
+    // lane offsets of the copies of a whole 16-row sub-tile (copy_rows' map with valid = 16)
+    unsigned soff[SPARSE ? 1 : kDmaA];
+    if constexpr (!SPARSE) {
+#pragma unroll
+        for (int i = 0; i < kDmaA; ++i) {
+            const int q = i * 64 + lane;
+            int r = (int)(__umul24((unsigned)q, 898u) >> 16);
+            int c = q - kRowSlots * r;
+            r = r < 16 ? r : 0;
+            c = c < kChunks ? c : 0;
+            soff[i] = (unsigned)(r * kRowBytes + c * 16);
+        }
+    }
     auto issue = [&](int k) {
         const int tok = tok_begin + 16 * (wave + 4 * k);
         if constexpr (SPARSE) {
@@ -267,7 +280,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
                                    p.nblocks);
         const unsigned char* gbase = (const unsigned char*)p.kcache + (size_t)page * kPageBytes +
                                      (size_t)(tok & 63) * kRowBytes;
-        copy_rows(gbase, min(16, tok_end - tok), slot0 + (unsigned)(k & 1) * kSlotA, 0, 1, kDmaA, lane);
+        const unsigned dst = slot0 + (unsigned)(k & 1) * kSlotA;
+        if (tok_end - tok >= 16) {
+#pragma unroll
+            for (int i = 0; i < kDmaA; ++i) dma16s(gbase, soff[i], dst + (unsigned)i * 1024u);
+        } else {
+            copy_rows(gbase, tok_end - tok, dst, 0, 1, kDmaA, lane);
+        }
     };
 
     // Prologue. Every wave's first slot is issued first; the workgroup's 16
@@ -406,6 +425,23 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
 // S^T tiles / P^T operand: elements 0-3 are tile 0 rows 4g..4g+3, 4-7 tile 1
 __device__ __forceinline__ int f8_token(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
 
+// Lane map of copy i of a slot: position pos = 64 i + lane holds chunk c of row
+// r, where pp = pos minus the pad chunk before row 16, r = pp / 37 (exact as
+// (pp * 1772) >> 16 for pp < 2367), c = pp mod 37; pad chunks and rows >= valid
+// read the run's first chunk. The scale positions of the last copy get the
+// byte offset of their four scales in the run's scale array instead.
+__device__ __forceinline__ unsigned f8_stream_offset(int i, int lane, int valid)
+{
+    const int pos = i * 64 + lane;
+    if (pos >= kF8Scale && pos < kF8Scale + 8) return (unsigned)(16 * (pos - kF8Scale));
+    const int pp = pos - (pos >= kF8Row16 ? 1 : 0);
+    int r = (int)(__umul24((unsigned)pp, 1772u) >> 16);
+    const int c = pp - kF8Chunks * r;
+    const bool data = pos != kF8Row16 - 1 && c < 36 && r < 32;
+    r = r < valid ? r : 0;
+    return data ? (unsigned)(r * kDqk + 16 * c) : 0u;
+}
+
 __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsA];
@@ -438,6 +474,12 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
     for (int nt = 0; nt < 32; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const unsigned slot0 = lds0 + (unsigned)(2 * wave) * kSlotA;
+    // lane offsets of the copies of a whole 32-row sub-tile; in the last copy the
+    // lanes at the scale positions (fscl) take their offset from the run's scales
+    unsigned foff[kDmaA];
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i) foff[i] = f8_stream_offset(i, lane, 32);
+    const bool fscl = (kDmaA - 1) * 64 + lane >= kF8Scale && (kDmaA - 1) * 64 + lane < kF8Scale + 8;
     auto issue = [&](int k) {
         const int tok = tok_begin + 32 * (wave + 4 * k);
         const int pidx = (tok >> 6) - j0;
@@ -449,25 +491,19 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
         const unsigned char* sbase = (const unsigned char*)(p.kscale + row0);
         const int valid = min(32, tok_end - tok);
         const unsigned dst = slot0 + (unsigned)(k & 1) * kSlotA;
-        // Branch-free lane map: position pos holds chunk c of row r, where
-        // pp = pos minus the pad chunk before row 16, r = pp / 37 (exact as
-        // (pp * 1772) >> 16 for pp < 2367), c = pp mod 37; pad chunks and rows
-        // >= valid read the run's first chunk, the last copy also the scales.
+        if (valid == 32) {
+#pragma unroll
+            for (int i = 0; i < kDmaA - 1; ++i) dma16s(gbase, foff[i], dst + (unsigned)i * 1024u);
+            dma16(fscl ? sbase + foff[kDmaA - 1] : gbase + foff[kDmaA - 1], dst + (unsigned)(kDmaA - 1) * 1024u);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < kDmaA; ++i) {
-            const int pos = i * 64 + lane;
-            const int pp = pos - (pos >= kF8Row16 ? 1 : 0);
-            int r = (int)(__umul24((unsigned)pp, 1772u) >> 16);
-            const int c = pp - kF8Chunks * r;
-            const bool data = pos != kF8Row16 - 1 && c < 36 && r < 32;
-            r = r < valid ? r : 0;
-            const unsigned off = data ? (unsigned)(r * kDqk + 16 * c) : 0u;
-            if (i == kDmaA - 1) {
-                const bool scl = pos >= kF8Scale && pos < kF8Scale + 8;
-                dma16(scl ? sbase + 16 * (pos - kF8Scale) : gbase + off, dst + (unsigned)i * 1024u);
-            } else {
+            const unsigned off = f8_stream_offset(i, lane, valid);
+            if (i == kDmaA - 1)
+                dma16(fscl ? sbase + off : gbase + off, dst + (unsigned)i * 1024u);
+            else
                 dma16s(gbase, off, dst + (unsigned)i * 1024u);
-            }
         }
     };
 
