@@ -312,6 +312,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
         const unsigned qa = qslot + (unsigned)(c16 * kLdsRow + 16 * g);
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) qf[0][ks] = __builtin_bit_cast(bf16x8, lds_load16(qa + 64 * ks));
+        // the queries live in AGPRs, which the matrix ops read directly (left to the
+        // register allocator they are parked there and copied back every step)
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+a"(qf[0][ks]));
     }
     wg_barrier();                                           // every wave holds its queries
     if (wave == 3 && K > 1) issue(1);
@@ -526,6 +530,8 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
         const unsigned qa = qslot + (unsigned)(c16 * kLdsRow + 16 * g);
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, lds_load16(qa + 64 * ks));
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+a"(qf[ks]));       // in AGPRs, as above
     }
     wg_barrier();
     if (wave == 3 && K > 1) issue(1);
