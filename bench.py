@@ -45,7 +45,7 @@ MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "mla_paged_latent_amd", "csrc")
 DECODE_SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_decode_wide.hip", "mla_decode_wide_fp8.hip",
                                                 "mla_device.h", "mla_common.h")]
-APPEND_SRCS = [os.path.join(CSRC, f) for f in ("mla_append.hip", "mla_common.h")]
+APPEND_SRCS = [os.path.join(CSRC, f) for f in ("mla_append.hip", "mla_device.h", "mla_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

@@ -9,7 +9,10 @@
 //
 //  * append_kernel: one wave per new row; the row's 1152 bytes are 72 chunks
 //    of 16 B, lanes 0-63 take chunks 0-63 and lanes 0-7 also 64-71, so the
-//    reads and the writes are whole 1 KB + 128 B runs.
+//    reads and the writes are whole 1 KB + 128 B runs. The new row is loaded
+//    before (and beside) the sequence length and the block-table entry that
+//    place it, which are wave-uniform scalar loads: two memory round trips per
+//    row instead of three.
 //  * BlockPool: host bookkeeping only (no HIP call): a LIFO free list of
 //    physical block ids and, per sequence, its length and blocks in order.
 #include <stdint.h>
@@ -19,7 +22,7 @@
 #include <vector>
 
 #include "../../include/mla_paged_latent.h"
-#include "mla_common.h"
+#include "mla_device.h"
 
 namespace mla {
 namespace {
@@ -33,20 +36,22 @@ __global__ __launch_bounds__(256) void append_kernel(uint16_t* __restrict__ kcac
                                                      const uint16_t* __restrict__ rows, int batch, int s_new)
 {
     const int lane = threadIdx.x & 63;
-    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);   // new row b * s_new + i
+    const long r = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // new row b * s_new + i
     if (r >= (long)batch * s_new) return;
+    // the row first (it needs nothing else); lanes 8-63 re-read chunks 64-71 of the
+    // row, so the load is unconditional and nothing waits on it before the stores
+    const u32x4a* src = (const u32x4a*)(rows + (size_t)r * kDqk);
+    const u32x4a a = src[lane];
+    const u32x4a c = src[64 + (lane & 7)];
     const int b = (int)(r / s_new);
     const int i = (int)(r - (long)b * s_new);
-    const int pos = seqlens[b] - s_new + i;                      // its token position
-    if (pos < 0) return;                                         // sequence shorter than s_new
-    if ((pos >> 6) >= max_blocks) return;                        // past the table: not written
-    const int page = block_table[(size_t)b * max_blocks + (pos >> 6)];
-    if (page < 0 || page >= nblocks) return;                     // not a block of the cache: not written
-    const u32x4a* src = (const u32x4a*)(rows + (size_t)r * kDqk);
+    const int pos = cload(seqlens + b) - s_new + i;              // its token position
+    // rows of a sequence shorter than s_new, past the table or in a block outside
+    // the cache are not written (the table is read at a valid index regardless)
+    const bool in_table = pos >= 0 && (pos >> 6) < max_blocks;
+    const int page = cload(block_table + (size_t)b * max_blocks + (in_table ? (pos >> 6) : 0));
+    if (!in_table || page < 0 || page >= nblocks) return;
     u32x4a* dst = (u32x4a*)(kcache + ((size_t)page * kPage + (pos & (kPage - 1))) * kDqk);
-    const u32x4a a = src[lane];
-    u32x4a c = {0u, 0u, 0u, 0u};
-    if (lane < 8) c = src[64 + lane];
     dst[lane] = a;
     if (lane < 8) dst[64 + lane] = c;
 }
@@ -64,19 +69,19 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(unsigned char* __restri
                                                          const uint16_t* __restrict__ rows, int batch, int s_new)
 {
     const int lane = threadIdx.x & 63;
-    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long r = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (r >= (long)batch * s_new) return;
+    const u32x4a* src = (const u32x4a*)(rows + (size_t)r * kDqk);
+    const u32x4a a = src[lane];                                  // the row first, as in append_kernel
+    const u32x4a c8 = src[64 + (lane & 7)];
+    const u32x4a c = lane < 8 ? c8 : u32x4a{0u, 0u, 0u, 0u};
     const int b = (int)(r / s_new);
     const int i = (int)(r - (long)b * s_new);
-    const int pos = seqlens[b] - s_new + i;
-    if (pos < 0 || (pos >> 6) >= max_blocks) return;
-    const int page = block_table[(size_t)b * max_blocks + (pos >> 6)];
-    if (page < 0 || page >= nblocks) return;
+    const int pos = cload(seqlens + b) - s_new + i;
+    const bool in_table = pos >= 0 && (pos >> 6) < max_blocks;
+    const int page = cload(block_table + (size_t)b * max_blocks + (in_table ? (pos >> 6) : 0));
+    if (!in_table || page < 0 || page >= nblocks) return;
     const size_t drow = (size_t)page * kPage + (pos & (kPage - 1));
-    const u32x4a* src = (const u32x4a*)(rows + (size_t)r * kDqk);
-    const u32x4a a = src[lane];
-    u32x4a c = {0u, 0u, 0u, 0u};
-    if (lane < 8) c = src[64 + lane];
     float x[16];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
