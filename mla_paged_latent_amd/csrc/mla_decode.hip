@@ -235,16 +235,22 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     }
 
     const unsigned slot0 = lds0 + (unsigned)(2 * wave) * kSlotA;
-    // lane offsets of the copies of a whole 16-row sub-tile (copy_rows' map with valid = 16)
-    unsigned soff[SPARSE ? 1 : kDmaA];
-    if constexpr (!SPARSE) {
+    // lane offsets of the copies of a whole 16-row sub-tile (copy_rows' map with valid = 16);
+    // SPARSE: the lane's byte offset within its row, and in bit i of `second` whether
+    // the lane of copy i takes the copy's second row
+    unsigned soff[kDmaA];
+    unsigned second = 0;
 #pragma unroll
-        for (int i = 0; i < kDmaA; ++i) {
-            const int q = i * 64 + lane;
-            int r = (int)(__umul24((unsigned)q, 898u) >> 16);
-            int c = q - kRowSlots * r;
+    for (int i = 0; i < kDmaA; ++i) {
+        const int q = i * 64 + lane;
+        int r = (int)(__umul24((unsigned)q, 898u) >> 16);
+        int c = q - kRowSlots * r;
+        c = c < kChunks ? c : 0;
+        if constexpr (SPARSE) {
+            soff[i] = (unsigned)(c * 16);
+            second |= (r != (i * 64) / kRowSlots ? 1u : 0u) << i;
+        } else {
             r = r < 16 ? r : 0;
-            c = c < kChunks ? c : 0;
             soff[i] = (unsigned)(r * kRowBytes + c * 16);
         }
     }
@@ -260,17 +266,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
                 rid = *(const __attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)(tok - tok_begin + lane));
             rid = rid >= 0 ? rid : fallback;
             const unsigned char* kc = (const unsigned char*)p.kcache;
-#pragma unroll 1
+#pragma unroll
             for (int i = 0; i < kDmaA; ++i) {
-                const int q = i * 64 + lane;
-                const int r = (int)(__umul24((unsigned)q, 898u) >> 16);
-                int c = q - kRowSlots * r;
-                c = c < kChunks ? c : 0;
                 const int r0 = (i * 64) / kRowSlots;
                 const int r1 = r0 + 1 < 16 ? r0 + 1 : 0;             // slot positions past row 15: any real row
                 const unsigned char* base0 = kc + (size_t)__builtin_amdgcn_readlane(rid, r0) * kRowBytes;
                 const unsigned char* base1 = kc + (size_t)__builtin_amdgcn_readlane(rid, r1) * kRowBytes;
-                dma16((r == r0 ? base0 : base1) + c * 16, dst + (unsigned)i * 1024u);
+                dma16((((second >> i) & 1u) ? base1 : base0) + soff[i], dst + (unsigned)i * 1024u);
             }
             return;
         }
