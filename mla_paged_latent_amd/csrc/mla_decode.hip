@@ -202,14 +202,23 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p)
     if constexpr (SPARSE) {
         const int32_t* list = p.indices + (size_t)b * p.topk;
         const int32_t* rtable = p.block_table + (size_t)(b / p.sq_real) * p.max_blocks;
-        for (int e = (int)threadIdx.x; e < tok_end - tok_begin; e += 256) {
-            const int t = list[tok_begin + e];
-            int rowid = -1;
-            if (t >= 0 && (t >> 6) < p.max_blocks) {
-                const int pg = rtable[t >> 6];
-                if (pg >= 0 && (int64_t)pg < p.nblocks) rowid = pg * kPage + (t & (kPage - 1));
-            }
-            *(__attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)e) = rowid;
+        // every list entry of the thread first, then every table entry they name: two
+        // memory round trips in all rather than two per entry
+        constexpr int kPer = kMaxTopk / 256;
+        const int nent = tok_end - tok_begin;
+        int t[kPer], pg[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = (int)threadIdx.x + 256 * j;
+            t[j] = e < nent ? list[tok_begin + e] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) pg[j] = (t[j] >= 0 && (t[j] >> 6) < p.max_blocks) ? rtable[t[j] >> 6] : -1;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = (int)threadIdx.x + 256 * j;
+            const int rowid = (pg[j] >= 0 && (int64_t)pg[j] < p.nblocks) ? pg[j] * kPage + (t[j] & (kPage - 1)) : -1;
+            if (e < nent) *(__attribute__((address_space(3))) int*)(uintptr_t)(rowtab + 4u * (unsigned)e) = rowid;
         }
         settle_loads();
         wg_barrier();
