@@ -193,8 +193,9 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
             f32x16 s0, s1;
 #pragma unroll
             for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-            {
-                const bool spread = more && whole;
+            // (two copies of the loop, with and without the spread copies, so that no
+            // branch sits between its matrix ops)
+            auto qk = [&](auto with_copy) {
                 u32x2 kv[4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) kv[ks] = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(sb + k_base + 16u * ks);
@@ -208,10 +209,15 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
                     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[ks & 1], qf[1][ks], s1, 0, 0, 0);
                     if (ks + 1 < 18) a2[(ks + 1) & 1] = e4m3x8_to_bf16(kv[(ks + 1) & 3]);
                     if (ks + 4 < 18) kv[ks & 3] = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(sb + k_base + 16u * (ks + 4));
-                    if (ks < 10 && spread) copy_one(ks, coff[ks]);
+                    if constexpr (decltype(with_copy)::value)
+                        if (ks < 10) copy_one(ks, coff[ks]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            if (more && whole)
+                qk(std::true_type{});
+            else
+                qk(std::false_type{});
             if (more) copy_end();
             // row scales of the owned tile's tokens (element i: token 32 th + token_of_row(8(i/4) + 4h + i%4)
             // of the block), read here so that their latency passes under the exchange barrier
