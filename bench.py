@@ -43,9 +43,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
 MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "mla_paged_latent_amd", "csrc")
-DECODE_SRCS = [os.path.join(CSRC, f) for f in ("mla_decode.hip", "mla_decode_wide.hip", "mla_decode_wide_fp8.hip",
-                                                "mla_device.h", "mla_common.h")]
-APPEND_SRCS = [os.path.join(CSRC, f) for f in ("mla_append.hip", "mla_device.h", "mla_common.h")]
+# the sources each benchmark case's dominant kernel is built from (its own file and the shared headers)
+KERNEL_SRCS = {
+    "decode_wide_kernel": ("mla_decode_wide.hip", "mla_device.h", "mla_common.h"),
+    "decode_wide_fp8_kernel": ("mla_decode_wide_fp8.hip", "mla_device.h", "mla_common.h"),
+    "stream": ("mla_decode.hip", "mla_device.h", "mla_common.h"),
+    "append": ("mla_append.hip", "mla_device.h", "mla_common.h"),
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -74,9 +78,13 @@ def traffic_kernel(key: str) -> str:
 
 
 def kernel_source_digest(key: str = "memory_bound") -> str:
+    """Digest of the sources of a case's dominant kernel: its traffic counters stay valid
+    while these files are unchanged."""
+    kname = traffic_kernel(key)
+    files = KERNEL_SRCS.get(kname) or KERNEL_SRCS["append" if key.startswith("append") else "stream"]
     h = hashlib.sha256()
-    for path in (APPEND_SRCS if key.startswith("append") else DECODE_SRCS):
-        with open(path, "rb") as f:
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
