@@ -43,11 +43,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
 MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "mla_paged_latent_amd", "csrc")
-# the sources each benchmark case's dominant kernel is built from (its own file and the shared headers)
+# the sources that decide each benchmark case's dominant kernel and its traffic: the kernel's own file, the
+# shared headers and, for the decode kernels, the plan and its sizing (they set the split partials it writes)
+PLAN_SRCS = ("mla_plan.hip", "mla_api.hip")
 KERNEL_SRCS = {
-    "decode_wide_kernel": ("mla_decode_wide.hip", "mla_device.h", "mla_common.h"),
-    "decode_wide_fp8_kernel": ("mla_decode_wide_fp8.hip", "mla_device.h", "mla_common.h"),
-    "stream": ("mla_decode.hip", "mla_device.h", "mla_common.h"),
+    "decode_wide_kernel": ("mla_decode_wide.hip", "mla_device.h", "mla_common.h") + PLAN_SRCS,
+    "decode_wide_fp8_kernel": ("mla_decode_wide_fp8.hip", "mla_device.h", "mla_common.h") + PLAN_SRCS,
+    "stream": ("mla_decode.hip", "mla_device.h", "mla_common.h") + PLAN_SRCS,
     "append": ("mla_append.hip", "mla_device.h", "mla_common.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")

@@ -77,7 +77,9 @@ const char* mla_status_string(int status);
  *     in [16, 1024].
  *   num_cus: compute units to plan for; <= 0 asks the current HIP device.
  * Outputs (any may be NULL):
- *   num_units: work units the plan splits the batch into (pass it to both calls);
+ *   num_units: work units the plan splits the batch into (pass it to both calls):
+ *     num_cus / head groups for the 64-row kernels, (num_cus - num_cus / 8) /
+ *     head groups but at least batch + 1 for the 16-row kernels;
  *   meta_bytes: bytes of tile_meta (int32 [num_units, MLA_META_INTS]);
  *   splits_bytes: bytes of num_splits (int32 [batch + 1]);
  *   workspace_bytes: bytes of the split-KV workspace mla_decode_fwd needs.

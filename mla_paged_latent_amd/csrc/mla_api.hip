@@ -144,9 +144,12 @@ int mla_plan_sizes(int batch, int s_q, int h_q, int num_cus, int* num_units, siz
         if (num_cus <= 0) return MLA_ERR_HIP;
     }
     const Geometry geo = geometry(s_q, h_q);
-    // one workgroup per CU (the block buffers fill most of the LDS); a
-    // per-sequence plan needs at least one unit per sequence and one to spare
-    int units = num_cus / geo.head_groups;
+    // one workgroup per CU (the block buffers fill most of the LDS); the 16-row
+    // kernels' per-sequence plans take 7/8 of the CUs (fewer, longer units: fewer
+    // split partials to write and merge, and the remaining CUs still saturate
+    // HBM), and need at least one unit per sequence and one to spare
+    const int cus = geo.by_sequence ? num_cus - num_cus / 8 : num_cus;
+    int units = cus / geo.head_groups;
     if (units < 1) units = 1;
     if (geo.by_sequence && units < batch + 1) units = batch + 1;
     size_t part_o = 0, total = 0;

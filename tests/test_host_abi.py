@@ -121,10 +121,11 @@ def test_get_metadata_rejects_bad_arguments(lib):
 
 
 def test_plan_sizes(lib):
+    # 16 query rows per workgroup: 7/8 of the CUs
     s = mla.mla_plan_sizes(16, 1, 16, num_cus=256)
-    assert s["num_units"] == 256
-    assert s["meta_bytes"] == 256 * 8 * 4 and s["splits_bytes"] == 17 * 4
-    assert s["workspace_bytes"] == mla.mla_workspace_bytes(16, 1, 16, 256)
+    assert s["num_units"] == 224
+    assert s["meta_bytes"] == 224 * 8 * 4 and s["splits_bytes"] == 17 * 4
+    assert s["workspace_bytes"] == mla.mla_workspace_bytes(16, 1, 16, 224)
     assert mla.mla_plan_sizes(300, 1, 16, num_cus=256)["num_units"] == 301
     # 64 query rows per workgroup: h_q=128, s_q=2 is 256 rows = four head groups
     assert mla.mla_plan_sizes(128, 2, 128, num_cus=256)["num_units"] == 64
@@ -132,8 +133,8 @@ def test_plan_sizes(lib):
     # 192 rows = three head groups
     assert mla.mla_plan_sizes(64, 3, 64, num_cus=256)["num_units"] == 85
     assert mla.mla_plan_sizes(64, 1, 64, num_cus=256)["num_units"] == 256
-    # 48 rows: three head groups of 16, per-sequence plan
-    assert mla.mla_plan_sizes(8, 3, 16, num_cus=256)["num_units"] == 85
+    # 48 rows: three head groups of 16, per-sequence plan (224 CUs' worth)
+    assert mla.mla_plan_sizes(8, 3, 16, num_cus=256)["num_units"] == 74
     with pytest.raises(mla.MLAError):
         mla.mla_plan_sizes(4, 1, 10, num_cus=256)
 
