@@ -27,6 +27,17 @@
 namespace mla {
 namespace {
 
+// Max over the lane's 16-lane row with DPP (quad swaps, then the 8- and 16-lane
+// mirrors), all in registers.
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));   // quad [1,0,3,2]
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));   // quad [2,3,0,1]
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true)));  // row half mirror
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true)));  // row mirror
+    return x;
+}
+
 typedef unsigned u32x4a __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2a __attribute__((ext_vector_type(2)));
 
@@ -61,7 +72,8 @@ __global__ __launch_bounds__(256) void append_kernel(uint16_t* __restrict__ kcac
 // scale = amax / 448 and codes = E4M3(x * (448 / amax)), both quotients
 // correctly rounded float32 and the product one float32 multiply, converted
 // to E4M3 by the hardware (round to nearest even; |x * 448 / amax| <= 448 so
-// nothing saturates). A zero row gets scale 0 and codes 0.
+// nothing saturates). A zero row gets scale 0 and codes 0. The wave max is
+// taken in registers (DPP within 16-lane rows, then lane swaps across rows).
 __global__ __launch_bounds__(256) void append_fp8_kernel(unsigned char* __restrict__ codes, float* __restrict__ scales,
                                                          int64_t nblocks,
                                                          const int32_t* __restrict__ block_table, int max_blocks,
@@ -93,8 +105,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(unsigned char* __restri
     float m = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(x[k]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    m = xor32_max(xor16_max(row16_max(m)));                      // the row's largest magnitude, in every lane
     const float inv = m > 0.f ? __fdiv_rn(448.f, m) : 0.f;
     unsigned w[4];
 #pragma unroll
