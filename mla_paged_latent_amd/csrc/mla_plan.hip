@@ -20,15 +20,19 @@ constexpr int kPlanThreads = 1024;       // largest workgroup; small batches lau
 // finishes sooner with fewer waves to synchronise, a large one needs them all.
 inline int plan_threads(int batch) { return batch <= 1024 ? 256 : kPlanThreads; }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// Inclusive prefix sum across the 64 lanes of a wave, in registers with DPP:
+// shifts by 1, 2, 4 and 8 within each 16-lane row (lanes shifted in from
+// outside the row add 0), then the total of row 0 is added to row 1 and that
+// of row 2 to row 3 (row_bcast:15), then the total of rows 0-1 to rows 2-3
+// (row_bcast:31).
 __device__ __forceinline__ int wave_inclusive_scan(int x)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
     return x;
 }
 
@@ -96,7 +100,7 @@ __device__ void plan_small(const int32_t* __restrict__ seqlens, int batch, int r
     const int kappa = by_seq ? 0 : kSegmentCost;
     const int cost = nb > 0 ? nb + kappa : 0;
     const int pin = wave_inclusive_scan(cost);
-    const int total = __shfl(pin, 63, 64);
+    const int total = __builtin_amdgcn_readlane(pin, 63);
     const int W = by_seq ? plan_width(total, num_units - batch) : plan_width(total, num_units);
     const int ns = lane < batch ? (by_seq ? ceil_div(nb, W) : plan_splits(pin - cost, nb, kappa, W)) : 0;
     const int nsin = wave_inclusive_scan(ns);
