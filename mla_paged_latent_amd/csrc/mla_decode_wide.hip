@@ -65,10 +65,24 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     const unsigned xin = lds0 + 2 * kBlockB;                // inbox of wave 0
     const unsigned xmine = xin + (unsigned)wave * kXB;
 
+    // Block-table window of the copy cursor: lane i holds entry tw_j + i of
+    // sequence tw_b (loaded speculatively for the unit's first block before
+    // its segment is known). A window is loaded where the cursor leaves the
+    // previous one and read (readlane) only at the next block's copies, after
+    // the wait for the block in flight, so the load never stalls a wave.
+    int tw_b = b0, tw_j = j0;
+    int tabv = b0 < p.batch ? table_window(p, tw_b, tw_j, lane) : 0;
     Segment is = next_segment(p, b0, b0, j0, b1, j1);      // copy cursor
     if (is.b >= p.batch) return;
     int itok = is.tb;
-    int ipage = table_page(p, is.b, itok >> 6);
+    auto cover = [&]() {                                    // the window holds the cursor's block
+        if (is.b != tw_b || (itok >> 6) - tw_j >= 64) {
+            tw_b = is.b;
+            tw_j = itok >> 6;
+            tabv = table_window(p, tw_b, tw_j, lane);
+        }
+    };
+    cover();
     Segment cs = is;                                        // compute cursor
 
     // This wave's copies of a block: copy i = wave + 4k of each half (36 per
@@ -84,7 +98,10 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     int n_issued = 0;
     // The next block of the copy cursor goes to LDS block (n_issued % 2):
     // copy_src / copy_dst give the global page and this wave's LDS base.
-    auto copy_src = [&]() { return (const unsigned char*)p.kcache + (size_t)ipage * kPageBytes; };
+    auto copy_src = [&]() {
+        const int page = safe_page(__builtin_amdgcn_readlane(tabv, (itok >> 6) - tw_j), p.nblocks);
+        return (const unsigned char*)p.kcache + (size_t)page * kPageBytes;
+    };
     auto copy_dst = [&]() { return lds0 + (unsigned)(n_issued & 1) * kBlockB + (unsigned)wave * 1024u; };
     // copy k (0..17) of a whole block: half k / 9, copy k % 9 of that half
     auto copy_full = [&](const unsigned char* gbase, unsigned dst, int k) {
@@ -99,7 +116,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
             is = next_segment(p, is.b + 1, b0, j0, b1, j1);
             itok = is.tb;
         }
-        if (is.b < p.batch) ipage = table_page(p, is.b, itok >> 6);
+        if (is.b < p.batch) cover();
     };
     // Copy the next block all at once. Rows past the segment's end are copied
     // from the block's first row (finite data, masked to p = 0).
@@ -153,6 +170,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
     while (cs.b < p.batch) {
         // new segment: this wave's column half of Q for both row groups (qf[0]:
         // the owned group kh, qf[1]: the other), fresh softmax state
+        const int sp0 = cload(p.splits + cs.b), sp1 = cload(p.splits + cs.b + 1);
         bf16x8 qf[2][18];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
@@ -165,6 +183,10 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
         for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+a"(qf[rg][ks]));
+        // (the split counts are needed only at the segment's end; taking them
+        // here, after the query loads, keeps the block loop free of pending
+        // scalar loads, which would make its LDS waits wait for everything)
+        asm volatile("" : : "s"(sp0), "s"(sp1));
         f32x16 acc[2][4];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg)
@@ -330,8 +352,8 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
         // ---- end of segment: row sums of both token halves, then this wave's 128 dims of 64 rows
         if (h == 0) *(lds_f32*)(uintptr_t)(xmine + kXSum + 4u * r32) = lrun;
         wg_barrier();
-        const int nsplit = sload(p.splits + cs.b + 1) - sload(p.splits + cs.b);
-        const int slot = cs.b == b0 ? first_slot : sload(p.splits + cs.b);
+        const int nsplit = sp1 - sp0;
+        const int slot = cs.b == b0 ? first_slot : sp0;
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
             const float lt = lds_f(xin + (unsigned)rg * kXB + kXSum + 4u * r32) +

@@ -97,11 +97,29 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
     const unsigned xmine = xin + (unsigned)wave * kXBf;
     const unsigned scl0 = xin + 4 * kXBf;                   // row scales of LDS block 0 (block 1: + kScaleB)
 
+    // Block-table window of the copy cursor: lane i holds entry tw_j + i of
+    // sequence tw_b (loaded speculatively for the unit's first block before
+    // its segment is known). A window is loaded where the cursor leaves the
+    // previous one and read (readlane) only at the next block's copies, after
+    // the wait for the block in flight, so the load never stalls a wave.
+    int tw_b = b0, tw_j = j0;
+    int tabv = b0 < p.batch ? table_window(p, tw_b, tw_j, lane) : 0;
     Segment is = next_segment(p, b0, b0, j0, b1, j1);   // copy cursor
     if (is.b >= p.batch) return;
     int itok = is.tb;
-    int ipage = table_page(p, is.b, itok >> 6);
+    auto cover = [&]() {                                   // the window holds the cursor's block
+        if (is.b != tw_b || (itok >> 6) - tw_j >= 64) {
+            tw_b = is.b;
+            tw_j = itok >> 6;
+            tabv = table_window(p, tw_b, tw_j, lane);
+        }
+    };
+    cover();
     Segment cs = is;                                       // compute cursor
+    // first cache row of the block at the copy cursor
+    auto copy_row0 = [&]() {
+        return (size_t)safe_page(__builtin_amdgcn_readlane(tabv, (itok >> 6) - tw_j), p.nblocks) * kPage;
+    };
 
     // this wave copies c = wave + 4k of each block's codes (10 copies for waves 0-1,
     // 9 for 2-3, whose last slot goes to the row scales: wave 2 copies them); the
@@ -111,8 +129,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
     for (int k = 0; k < 10; ++k) coff[k] = f8_copy_offset(kPage, wave + 4 * k, lane);
     int n_issued = 0;
     // copy k of this wave for the block at the copy cursor (k == ncopy: wave 2's row scales)
-    auto copy_one = [&](int k, unsigned off) {
-        const size_t row0 = (size_t)ipage * kPage;
+    auto copy_one = [&](int k, unsigned off, size_t row0) {
         if (k < 9 || wave < 2) {
             f8_block_copy(codes, row0, off, lds0 + (unsigned)(n_issued & 1) * kF8BlockB, wave + 4 * k);
         } else if (wave == 2 && lane < 16) {
@@ -127,11 +144,12 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
             is = next_segment(p, is.b + 1, b0, j0, b1, j1);
             itok = is.tb;
         }
-        if (is.b < p.batch) ipage = table_page(p, is.b, itok >> 6);
+        if (is.b < p.batch) cover();
     };
     {
         const int valid = is.te - itok;
-        for (int k = 0; k < 10; ++k) copy_one(k, f8_copy_offset(valid, wave + 4 * k, lane));
+        const size_t crow = copy_row0();
+        for (int k = 0; k < 10; ++k) copy_one(k, f8_copy_offset(valid, wave + 4 * k, lane), crow);
         copy_end();
     }
 
@@ -151,6 +169,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
     // scale of element i of the owned S^T tile: token token_of_row(8 (i / 4) + 4 h + i % 4) of the slot
     int n = 0;                                              // block being computed
     while (cs.b < p.batch) {
+        const int sp0 = cload(p.splits + cs.b), sp1 = cload(p.splits + cs.b + 1);
         bf16x8 qf[2][18];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
@@ -163,6 +182,10 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
         for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+a"(qf[rg][ks]));
+        // (the split counts are needed only at the segment's end; taking them
+        // here, after the query loads, keeps the block loop free of pending
+        // scalar loads, which would make its LDS waits wait for everything)
+        asm volatile("" : : "s"(sp0), "s"(sp1));
         f32x16 acc[2][4];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg)
@@ -184,7 +207,8 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
             const bool whole = is.te - itok >= kPage;
             if (more && !whole) {                           // the end of a segment: copied here
                 const int valid = is.te - itok;
-                for (int k = 0; k < 10; ++k) copy_one(k, f8_copy_offset(valid, wave + 4 * k, lane));
+                const size_t crow = copy_row0();
+                for (int k = 0; k < 10; ++k) copy_one(k, f8_copy_offset(valid, wave + 4 * k, lane), crow);
             }
             const unsigned blk = lds0 + (unsigned)(n & 1) * kF8BlockB;
             const unsigned sb = blk + (unsigned)th * kF8SlotB;
@@ -196,6 +220,8 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
             // (two copies of the loop, with and without the spread copies, so that no
             // branch sits between its matrix ops)
             auto qk = [&](auto with_copy) {
+                size_t crow = 0;
+                if constexpr (decltype(with_copy)::value) crow = copy_row0();
                 u32x2 kv[4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) kv[ks] = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(sb + k_base + 16u * ks);
@@ -210,7 +236,7 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
                     if (ks + 1 < 18) a2[(ks + 1) & 1] = e4m3x8_to_bf16(kv[(ks + 1) & 3]);
                     if (ks + 4 < 18) kv[ks & 3] = *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)(sb + k_base + 16u * (ks + 4));
                     if constexpr (decltype(with_copy)::value)
-                        if (ks < 10) copy_one(ks, coff[ks]);
+                        if (ks < 10) copy_one(ks, coff[ks], crow);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             };
@@ -334,8 +360,8 @@ __global__ __launch_bounds__(256) void decode_wide_fp8_kernel(DecodeParams p)
         // ---- end of segment: row sums of both token halves, then this wave's 128 dims of 64 rows
         if (h == 0) *(lds_f32*)(uintptr_t)(xmine + kXSumF + 4u * r32) = lrun;
         wg_barrier();
-        const int nsplit = sload(p.splits + cs.b + 1) - sload(p.splits + cs.b);
-        const int slot = cs.b == b0 ? first_slot : sload(p.splits + cs.b);
+        const int nsplit = sp1 - sp0;
+        const int slot = cs.b == b0 ? first_slot : sp0;
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
             const float lt = lds_ff(xin + (unsigned)rg * kXBf + kXSumF + 4u * r32) +

@@ -181,6 +181,15 @@ __device__ __forceinline__ int table_page(const DecodeParams& p, int b, int j)
     return j < p.max_blocks ? safe_page(cload(p.block_table + (size_t)b * p.max_blocks + j), p.nblocks) : 0;
 }
 
+// Entries j .. j + 63 of sequence b's block-table row, entry j + i in lane i
+// (0 past the row): a vector load, so its wait is counted with the block
+// copies rather than with the LDS operations.
+__device__ __forceinline__ int table_window(const DecodeParams& p, int b, int j, int lane)
+{
+    const int jj = j + lane;
+    return jj < p.max_blocks ? p.block_table[(size_t)b * p.max_blocks + jj] : 0;
+}
+
 // ---------------------------------------------------------------- units of the cost-line plan
 
 // The run of sequence b inside a unit: tokens [tb, te) of a sequence of L tokens.
