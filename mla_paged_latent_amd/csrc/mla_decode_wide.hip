@@ -37,6 +37,77 @@ constexpr int kLdsB = 2 * kBlockB + 4 * kXB;    // 163,840 B
 // (all 4 KB), afterwards its owner's row maxima, P^T tile and row sums.
 constexpr unsigned kXMax = 0, kXP = 128, kXSum = 2176;
 
+// Result rows.
+//
+// A lane of a 32x32 matrix-op output tile holds 16 dims of one row, so stores
+// straight from the accumulators would write 32 rows x 16 or 32 B per
+// instruction. The rows are staged row-major in LDS instead (one 16-byte pad
+// chunk per row spreads the lanes' writes of an instruction over the banks),
+// after which each store instruction writes 1 KB of one row.
+constexpr unsigned kStgB16 = 2 * kDv + 16;          // a staged bf16 row
+constexpr unsigned kStgF32 = 4 * kDv + 16;          // a staged fp32 row
+constexpr unsigned kStgBytes = 64 * kStgB16;        // 64 bf16 rows, or 32 fp32 rows
+static_assert(32 * kStgF32 <= kStgBytes, "fp32 staging fits");
+static_assert(kStgBytes <= kBlockB, "result staging fits a block buffer");
+
+// The 64 rows of a workgroup (rows_out: their first row in out, or in the split
+// partials when !final), acc[rg][dt][4 j + e] = dim 128 wave + 32 dt + 8 j + 4 h + e
+// of row 32 rg + r32, scaled by inv[rg]. stg: kStgBytes of LDS that no other
+// wave uses until the next workgroup barrier after this call.
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[2][4], const float (&inv)[2], unsigned stg,
+                                                  int wave, int lane, bool final, uint16_t* rows_out,
+                                                  float* rows_part)
+{
+    const int h = lane >> 5, r32 = lane & 31;
+    if (final) {
+        // bf16 rows; wave w then stores rows 16 w .. 16 w + 15
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x2 v;
+                    v[0] = pack_bf16x2(acc[rg][dt][4 * j + 0] * inv[rg], acc[rg][dt][4 * j + 1] * inv[rg]);
+                    v[1] = pack_bf16x2(acc[rg][dt][4 * j + 2] * inv[rg], acc[rg][dt][4 * j + 3] * inv[rg]);
+                    *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(
+                        stg + (unsigned)(32 * rg + r32) * kStgB16 + 2u * (unsigned)(128 * wave + 32 * dt + 8 * j + 4 * h)) = v;
+                }
+        wg_barrier();
+        uint16_t* o = rows_out + 8 * lane;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * wave + i;
+            *(s16x8*)(o + (size_t)r * kDv) = lds_load16(stg + (unsigned)r * kStgB16 + 16u * lane);
+        }
+    } else {
+        // fp32 rows, one row group at a time; wave w stores rows 8 w .. 8 w + 7 of it
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+            if (rg) wg_barrier();                           // every wave has stored the first group
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 v = {acc[rg][dt][4 * j + 0] * inv[rg], acc[rg][dt][4 * j + 1] * inv[rg],
+                                     acc[rg][dt][4 * j + 2] * inv[rg], acc[rg][dt][4 * j + 3] * inv[rg]};
+                    *(lds_f32x4*)(uintptr_t)(stg + (unsigned)r32 * kStgF32 +
+                                             4u * (unsigned)(128 * wave + 32 * dt + 8 * j + 4 * h)) = v;
+                }
+            wg_barrier();
+            float* o = rows_part + (size_t)(32 * rg) * kDv + 4 * lane;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * wave + i;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    *(f32x4*)(o + (size_t)r * kDv + 256 * hf) =
+                        *(const lds_f32x4*)(uintptr_t)(stg + (unsigned)r * kStgF32 + 1024u * hf + 16u * lane);
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ float lds_f(unsigned addr) { return *(const lds_f32*)(uintptr_t)addr; }
 
 __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
@@ -349,47 +420,32 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
             }
         }
 
-        // ---- end of segment: row sums of both token halves, then this wave's 128 dims of 64 rows
+        // ---- end of segment: row sums of both token halves, then the 64 result
+        // rows, staged in the LDS buffer of the segment's last block (free now:
+        // every wave is past its PV, and the block in flight goes to the other
+        // buffer).
         if (h == 0) *(lds_f32*)(uintptr_t)(xmine + kXSum + 4u * r32) = lrun;
         wg_barrier();
         const int nsplit = sp1 - sp0;
         const int slot = cs.b == b0 ? first_slot : sp0;
+        const unsigned stg = lds0 + (unsigned)((n - 1) & 1) * kBlockB;
+        float inv[2];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
             const float lt = lds_f(xin + (unsigned)rg * kXB + kXSum + 4u * r32) +
                              lds_f(xin + (unsigned)(rg + 2) * kXB + kXSum + 4u * r32);
-            const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            const int row = row0 + 32 * rg;
-            if (nsplit == 1) {
-                uint16_t* o = p.out + ((size_t)cs.b * p.rows_total + row) * kDv + 128 * wave + 4 * h;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        u32x2 v;
-                        v[0] = pack_bf16x2(acc[rg][dt][4 * j + 0] * inv, acc[rg][dt][4 * j + 1] * inv);
-                        v[1] = pack_bf16x2(acc[rg][dt][4 * j + 2] * inv, acc[rg][dt][4 * j + 3] * inv);
-                        *(u32x2*)(o + 32 * dt + 8 * j) = v;
-                    }
-            } else {
-                float* o = p.part_o + ((size_t)slot * p.rows_total + row) * kDv + 128 * wave + 4 * h;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        f32x4 v = {acc[rg][dt][4 * j + 0] * inv, acc[rg][dt][4 * j + 1] * inv,
-                                   acc[rg][dt][4 * j + 2] * inv, acc[rg][dt][4 * j + 3] * inv};
-                        *(f32x4*)(o + 32 * dt + 8 * j) = v;
-                    }
-            }
+            inv[rg] = lt > 0.f ? 1.f / lt : 0.f;
             if (wave == rg && h == 0) {
+                const int row = row0 + 32 * rg;
                 const float lse = lt > 0.f ? (mrun[rg] + __log2f(lt)) * kLn2 : -INFINITY;
                 if (nsplit == 1) p.lse[(size_t)cs.b * p.rows_total + row] = lse;
                 else p.part_lse[(size_t)slot * p.rows_total + row] = lse;
             }
         }
-        // (the next segment's query loads wait for these stores and the copy
-        // in flight; the next block's barrier keeps the row sums until all read them)
+        const size_t row_wg = (size_t)blockIdx.y * 64;      // the workgroup's first row
+        store_rows_staged(acc, inv, stg, wave, lane, nsplit == 1, p.out + ((size_t)cs.b * p.rows_total + row_wg) * kDv,
+                          p.part_o + ((size_t)slot * p.rows_total + row_wg) * kDv);
+        // (the next block's barrier keeps the row sums and the staged rows until all read them)
         cs = next_segment(p, cs.b + 1, b0, j0, b1, j1);
     }
 }
