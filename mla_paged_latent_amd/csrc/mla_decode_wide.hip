@@ -108,6 +108,17 @@ __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[2][4], con
     }
 }
 
+// Maximum for the row maxima: scores are finite or -inf here (masked tokens are
+// -inf, rows past a sequence's end hold finite copies), so the NaN-propagating
+// IEEE maximum (v_maximum3_f32) gives fmaxf's result without the NaN-quieting
+// operations fmaxf needs on values the compiler cannot prove canonical.
+__device__ __forceinline__ float fmaxr(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float xor32_maxr(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxr(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float lds_f(unsigned addr) { return *(const lds_f32*)(uintptr_t)addr; }
 
 __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
@@ -343,8 +354,8 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
             {
                 float m4[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) m4[j] = fmaxf(fmaxf(s[4 * j], s[4 * j + 1]), fmaxf(s[4 * j + 2], s[4 * j + 3]));
-                const float tmax = xor32_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * cs_);
+                for (int j = 0; j < 4; ++j) m4[j] = fmaxr(fmaxr(s[4 * j], s[4 * j + 1]), fmaxr(s[4 * j + 2], s[4 * j + 3]));
+                const float tmax = xor32_maxr(fmaxr(fmaxr(m4[0], m4[1]), fmaxr(m4[2], m4[3])) * cs_);
                 // (the inbox's score tile has been read: this wave's LDS ops run in order)
                 if (h == 0) *(lds_f32*)(uintptr_t)(xmine + kXMax + 4u * r32) = tmax;
             }
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeParams p)
             // ---- running max of all 64 rows (the same in every wave), lazy rescale
 #pragma unroll
             for (int rg = 0; rg < 2; ++rg) {
-                const float mb = fmaxf(lds_f(xin + (unsigned)rg * kXB + kXMax + 4u * r32),
+                const float mb = fmaxr(lds_f(xin + (unsigned)rg * kXB + kXMax + 4u * r32),
                                        lds_f(xin + (unsigned)(rg + 2) * kXB + kXMax + 4u * r32));
                 const bool need = mb > mrun[rg] + kLazyTau;
                 if (wave_any(need)) {
