@@ -45,8 +45,11 @@
 //    rescaled) only when a score exceeds it by more than 2^8, so P <= 256;
 //  * rows past the end of a sequence are loaded from the block's first valid
 //    row instead (finite data, masked to p = 0), so no LDS row holds garbage;
-//  * block-table entries and scalars are read with scalar loads so that they
-//    never wait on the vector-memory counter that tracks the block copies.
+//  * scalars (plan rows, sequence lengths, split counts) are read with scalar
+//    loads, and block-table entries 64 at a time with one vector load into a
+//    register (readlane picks an entry), awaited before the copy pipeline starts
+//    or together with a block copy that is awaited anyway, so that no wait in
+//    the pipeline is for anything but block copies.
 #include "mla_device.h"
 
 namespace mla {

@@ -174,13 +174,6 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b)
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Block j of sequence b from the block table (wave-uniform); an index past
-// the table or an entry outside [0, nblocks) gives block 0.
-__device__ __forceinline__ int table_page(const DecodeParams& p, int b, int j)
-{
-    return j < p.max_blocks ? safe_page(cload(p.block_table + (size_t)b * p.max_blocks + j), p.nblocks) : 0;
-}
-
 // Entries j .. j + 63 of sequence b's block-table row, entry j + i in lane i
 // (0 past the row): a vector load, so its wait is counted with the block
 // copies rather than with the LDS operations.
