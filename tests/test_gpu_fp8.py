@@ -109,6 +109,18 @@ def test_fp8_wide_plan_extremes(units):
     assert_parity(out, lse, ro, rl, "wide units %d" % units)
 
 
+@pytest.mark.parametrize("units", [1, 2])
+def test_fp8_wide_units_longer_than_a_table_window(units):
+    """The FP8 64-row kernel with units that walk more than 64 blocks of one sequence
+    (block-table window reloads inside a segment and at segment changes)."""
+    _say("fp8 wide, %d units over 141 + 79 + 2 blocks" % units)
+    inp = cases.small_batch([9000, 5040, 100], s_q=1, h_q=64, seed=240 + units)
+    codes, scales = fp8.quantize_rows(clean_rows(inp))
+    out, lse = run(inp, codes, scales, num_units=units)
+    ro, rl = ref(inp, codes, scales)
+    assert_parity(out, lse, ro, rl, "fp8 wide units %d" % units)
+
+
 @pytest.mark.parametrize("units", [17, 40, 900])
 def test_fp8_plan_extremes(units):
     _say("fp8 units=%d" % units)

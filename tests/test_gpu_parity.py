@@ -135,6 +135,19 @@ def test_plan_extremes_give_the_same_answer(h_q, units):
     assert_parity(out, lse, ref_out, ref_lse, "units=%d" % units)
 
 
+@pytest.mark.parametrize("units", [1, 2, 3])
+def test_wide_units_longer_than_a_table_window(units):
+    """64-row kernel with a few units over sequences of 141, 79 and 2 blocks: a unit
+    walks more than 64 blocks of one sequence (the copy cursor's 64-entry window of
+    the block table is reloaded inside a segment and at segment changes), and split
+    and unsplit sequences take both result-store paths (fp32 partials, bf16 rows)."""
+    inp = cases.small_batch([9000, 5040, 100], s_q=1, h_q=64, seed=230 + units)
+    _say("wide kernel, %d units over 141 + 79 + 2 blocks" % units)
+    out, lse, _ = run_library(inp, num_units=units)
+    ref_out, ref_lse = _oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, "wide units=%d" % units)
+
+
 def test_large_scores_stay_finite():
     inp = cases.small_batch([150, 1000], s_q=1, h_q=16, seed=21)
     inp.q[:] = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(inp.q) * 16.0)
