@@ -581,17 +581,26 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p)
         };
         f32x4 s[2];
         {
+            // K fragments are read four k-steps ahead and converted one step ahead
+            // (ping-pong), under the previous matrix op; a scheduling barrier per
+            // step keeps that order (left alone, the compiler paired the reads and
+            // waited for each pair two matrix ops after issuing it)
             u32x2 kr[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) kr[kk] = kread(kk);
             f32x4 e[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            bf16x8 a2[2];
+            a2[0] = e4m3x8_to_bf16(kr[0]);
 #pragma unroll
             for (int kk = 0; kk < 36; ++kk) {
+                __builtin_amdgcn_sched_barrier(0);
                 const int hh = kk / 18, ks = kk % 18;
-                e[2 * hh + (ks & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kr[kk & 3]), qf[ks],
-                                                                            e[2 * hh + (ks & 1)], 0, 0, 0);
+                e[2 * hh + (ks & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[kk & 1], qf[ks], e[2 * hh + (ks & 1)],
+                                                                            0, 0, 0);
+                if (kk + 1 < 36) a2[(kk + 1) & 1] = e4m3x8_to_bf16(kr[(kk + 1) & 3]);
                 if (kk + 4 < 36) kr[kk & 3] = kread(kk + 4);
             }
+            __builtin_amdgcn_sched_barrier(0);
             s[0] = e[0] + e[1];
             s[1] = e[2] + e[3];
         }
