@@ -725,6 +725,88 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p)
     if (t == 0) *lo = m + __logf(l);
 }
 
+// The combine for plans of 64-row workgroups, whose sequences have few splits
+// (two or three in the 64-row workloads): one wave per two rows, lane l merges
+// dims [8 l, 8 l + 8) of both rows, every partial of a pass in flight at once;
+// the partials' log-sum-exps are wave-uniform (scalar loads). The merge is
+// combine_kernel's, in passes of 8 partials instead of 16 (the same arithmetic
+// up to 8 splits). (With 16-row plans, whose sequences have up to dozens of
+// splits over few rows, this shape leaves too few waves in flight; they keep
+// combine_kernel.)
+__global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p)
+{
+    constexpr int U = 8;                                    // partials per pass
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int b = blockIdx.y;
+    const int s0 = cload(p.splits + b);
+    const int ns = cload(p.splits + b + 1) - s0;
+    if (ns == 1) return;
+    const int row0 = (blockIdx.x * 4 + wave) * 2;
+    if (row0 >= p.rows_total) return;
+    const bool two = row0 + 1 < p.rows_total;
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    f32x4 a[2][2] = {};
+    const float* lse_col = p.part_lse + (size_t)s0 * p.rows_total + row0;
+    const float* o_col = p.part_o + ((size_t)s0 * p.rows_total + row0) * kDv + 8 * lane;
+    for (int k = 0; k < ns; k += U) {
+        float w[2][U];
+        f32x4 v[2][U][2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                w[r][u] = -INFINITY;
+                v[r][u][0] = v[r][u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (k + u < ns && (r == 0 || two)) {
+                    w[r][u] = *(const __attribute__((address_space(4))) float*)(uintptr_t)(lse_col + (size_t)(k + u) * p.rows_total + r);
+                    const float* src = o_col + ((size_t)(k + u) * p.rows_total + r) * kDv;
+                    v[r][u][0] = *(const f32x4*)src;
+                    v[r][u][1] = *(const f32x4*)(src + 4);
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float mk = m[r];
+#pragma unroll
+            for (int u = 0; u < U; ++u) mk = fmaxf(mk, w[r][u]);
+            if (mk == -INFINITY) continue;                  // nothing visible yet
+            const float sc = __expf(m[r] - mk);             // 0 while m is -inf
+            l[r] *= sc;
+            a[r][0] *= sc;
+            a[r][1] *= sc;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float e = __expf(w[r][u] - mk);
+                l[r] += e;
+                a[r][0] += v[r][u][0] * e;
+                a[r][1] += v[r][u][1] * e;
+            }
+            m[r] = mk;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (r == 1 && !two) break;
+        const int row = row0 + r;
+        uint16_t* o = p.out + ((size_t)b * p.rows_total + row) * kDv + 8 * lane;
+        float* lo = p.lse + (size_t)b * p.rows_total + row;
+        if (m[r] == -INFINITY) {
+            *(u32x4*)o = u32x4{0u, 0u, 0u, 0u};
+            if (lane == 0) *lo = -INFINITY;
+            continue;
+        }
+        const float inv = 1.f / l[r];
+        u32x4 q;
+        q[0] = pack_bf16x2(a[r][0][0] * inv, a[r][0][1] * inv);
+        q[1] = pack_bf16x2(a[r][0][2] * inv, a[r][0][3] * inv);
+        q[2] = pack_bf16x2(a[r][1][0] * inv, a[r][1][1] * inv);
+        q[3] = pack_bf16x2(a[r][1][2] * inv, a[r][1][3] * inv);
+        *(u32x4*)o = q;
+        if (lane == 0) *lo = m[r] + __logf(l[r]);
+    }
+}
+
 hipError_t launch_decode(const DecodeParams& p, int num_units, int head_groups, int rows_wg, hipStream_t stream)
 {
     dim3 grid(num_units, head_groups);
@@ -745,8 +827,11 @@ hipError_t launch_decode_sparse(const DecodeParams& p, int num_units, int head_g
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream)
 {
-    dim3 grid((p.rows_total + 1) / 2, p.batch);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, p);
+    if (p.rows_total % 64 == 0) {
+        hipLaunchKernelGGL(combine_rows_kernel, dim3((p.rows_total + 7) / 8, p.batch), dim3(256), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL(combine_kernel, dim3((p.rows_total + 1) / 2, p.batch), dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
