@@ -459,6 +459,17 @@ def bench_sparse(args, torch, mla, dev):
         mla.mla_decode_sparse_fwd_splits(q, kc, table, idx, lens, d.softmax_scale, meta, splits, out=out, lse=lse,
                                          workspace=ws)
     kern_ms = graph_ms(torch, decode_only, args.steps)
+
+    def plan_only(k):
+        mla.mla_get_metadata_sparse(lens, B, s_q, h_q, topk, num_units=units, tile_meta=meta, num_splits=splits)
+
+    def decode_fwd(k):
+        kc, q = reps[k % R]
+        mla.mla_decode_sparse_fwd(q, kc, table, idx, lens, d.softmax_scale, meta, splits, out=out, lse=lse,
+                                  workspace=ws)
+    # the plan alone and the decode call alone (decode kernel + combine), K launches back to back
+    plan_ms = graph_ms(torch, plan_only, args.steps)
+    fwd_ms = graph_ms(torch, decode_fwd, args.steps)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
     result = {
@@ -470,7 +481,8 @@ def bench_sparse(args, torch, mla, dev):
                                "block_table, bf16 N(0,1), scale 1/sqrt(192)",
                    "batch": B, "s_q": s_q, "h_q": h_q, "topk": topk, "replicas": R, "num_units": units},
         "step": "mla_get_metadata_sparse + mla_decode_sparse_fwd (plan, decode kernel, split combine)",
-        "tflops": round(tf, 3), "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
+        "tflops": round(tf, 3), "plan_ms": round(plan_ms, 6), "decode_fwd_ms": round(fwd_ms, 6),
+        "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
         "roofline": kernel_roofline(mla, "sparse decode kernel (mla_decode_sparse_fwd_splits)", sp.counts, h_q, 1,
                                     units, nbytes, flops, kern_ms, measured_traffic("sparse"), plan_h_q=16),
     }
@@ -519,7 +531,8 @@ def bench_fp8(args, torch, mla, dev):
     reps = [(codes0.clone(), scales0.clone(), q0.clone(), table.clone(), lens.clone()) for _ in range(R)]
     del codes0, scales0, q0
     sizes = mla.mla_fp8_plan_sizes(B, s_q, h_q)
-    units = sizes["num_units"]
+    units = args.num_units or sizes["num_units"]
+    sizes["workspace_bytes"] = mla.mla_workspace_bytes(B, s_q, h_q, units)
     plans = [(torch.empty((units, mla.META_INTS), dtype=torch.int32, device=dev),
               torch.empty((B + 1,), dtype=torch.int32, device=dev)) for _ in range(R)]
     out = torch.empty((B, s_q, h_q, mla.D_V), dtype=torch.bfloat16, device=dev)
@@ -558,6 +571,19 @@ def bench_fp8(args, torch, mla, dev):
         mla.mla_decode_fp8_fwd_splits(q, c, sc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal,
                                       out=out, lse=lse, workspace=ws)
     kern_ms = graph_ms(torch, decode_only, args.steps)
+
+    def plan_only(k):
+        meta, splits = plans[k % R]
+        mla.mla_get_metadata_fp8(reps[k % R][4], h_q, s_q, num_units=units, tile_meta=meta, num_splits=splits)
+
+    def decode_fwd(k):
+        c, sc, q, tab, ln = reps[k % R]
+        meta, splits = plans[k % R]
+        mla.mla_decode_fp8_fwd(q, c, sc, tab, ln, inp.softmax_scale, meta, splits, causal=inp.causal, out=out,
+                               lse=lse, workspace=ws)
+    # the plan alone and the decode call alone (decode kernel + combine), K launches back to back
+    plan_ms = graph_ms(torch, plan_only, args.steps)
+    fwd_ms = graph_ms(torch, decode_fwd, args.steps)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
     result = {
@@ -571,7 +597,8 @@ def bench_fp8(args, torch, mla, dev):
                    "batch": B, "s_q": s_q, "h_q": h_q, "tokens": int(inp.cache_seqlens.sum()), "replicas": R,
                    "num_units": units},
         "step": "mla_get_metadata_fp8 + mla_decode_fp8_fwd (plan, decode kernel, split combine)",
-        "tflops": round(tf, 3), "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
+        "tflops": round(tf, 3), "plan_ms": round(plan_ms, 6), "decode_fwd_ms": round(fwd_ms, 6),
+        "alg_bytes_per_step": nbytes, "alg_flops_per_step": flops,
         "roofline": kernel_roofline(mla, "FP8 decode kernel (mla_decode_fp8_fwd_splits)", inp.cache_seqlens, h_q,
                                     s_q, units, nbytes, flops, kern_ms, measured_traffic("fp8_" + args.workload)),
     }
@@ -607,6 +634,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="mixed", choices=sorted(wl.WORKLOADS),
                     help="default: mixed, the largest single-GPU configuration")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 2x the 256 MB cache")
+    ap.add_argument("--num-units", type=int, default=0,
+                    help="decode / fp8: plan over this many units instead of the library's choice (0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="about the CPU-baseline leg's wall time")
     ap.add_argument("--no-context", action="store_true", help="skip the copy / GEMM ceiling measurements")
@@ -670,7 +699,8 @@ def main(argv=None):
     del base_k, base_q, base_t
 
     sizes = mla.mla_plan_sizes(B, s_q, h_q)
-    units = sizes["num_units"]
+    units = args.num_units or sizes["num_units"]
+    sizes["workspace_bytes"] = mla.mla_workspace_bytes(B, s_q, h_q, units)
     out = torch.empty((B, s_q, h_q, mla.D_V), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
     ws = torch.empty((sizes["workspace_bytes"],), dtype=torch.uint8, device=dev)
