@@ -135,6 +135,22 @@ def test_plan_extremes_give_the_same_answer(h_q, units):
     assert_parity(out, lse, ref_out, ref_lse, "units=%d" % units)
 
 
+@pytest.mark.parametrize("s_q,h_q,units", [(4, 16, 200), (4, 8, 200), (8, 128, 40)],
+                         ids=["64-row", "16-row", "1024-row"])
+def test_split_partials_that_see_no_token(s_q, h_q, units):
+    """Causal rows whose last split covers only tokens they may not see (a partial
+    with lse = -inf, weight 0 in the combine), and a sequence shorter than s_q whose
+    first new tokens see nothing at all (out = 0, lse = -inf); many units, so every
+    sequence is split at its blocks."""
+    inp = cases.small_batch([130, 2, 65, 200], s_q=s_q, h_q=h_q, seed=s_q * h_q + units)
+    _say("masked split partials s_q=%d h_q=%d units=%d" % (s_q, h_q, units))
+    out, lse, (meta, splits) = run_library(inp, num_units=units)
+    assert (np.diff(splits) > 1).sum() >= 2, "the plan should split the longer sequences"
+    ref_out, ref_lse = _oracle(inp)
+    assert np.isneginf(ref_lse).any(), "some query should see no token"
+    assert_parity(out, lse, ref_out, ref_lse, "masked partials")
+
+
 @pytest.mark.parametrize("units", [1, 2, 3])
 def test_wide_units_longer_than_a_table_window(units):
     """64-row kernel with a few units over sequences of 141, 79 and 2 blocks: a unit
